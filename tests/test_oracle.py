@@ -1,0 +1,443 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Page tag [P1] = "INT8ConvRot GEMM vs fp16 on M1 Max with Metal, MPSMatrix, and
+MLX (fp16 Wins)", section "What changed in the computation" unless stated.
+None of these checks retypes an oracle formula: they use a library routine
+(scipy's Sylvester Hadamard, numpy's IEEE casts), an independent algorithm (a
+textbook fast Walsh-Hadamard transform, exact rational arithmetic), closed
+forms derived by hand (tests/golden/hand_cases.json) or invariants.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from oracle import convrot_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _f32_from_bits(h: str) -> np.float32:
+    return np.array([int(h, 16)], dtype=np.uint32).view(np.float32)[0]
+
+
+def _popcount(v):
+    return bin(int(v)).count("1")
+
+
+# --------------------------------------------------------------------------- H
+
+def test_h4_is_sylvester():
+    # [P1]: "4x4 Hadamard matrices"; reading: Sylvester's, as scipy builds it.
+    assert np.array_equal(O.hadamard4(), scipy.linalg.hadamard(4))
+
+
+def test_h256_matches_library_sylvester():
+    assert np.array_equal(O.hadamard256_pm1(), scipy.linalg.hadamard(256))
+
+
+def test_h256_closed_form_popcount():
+    h = O.hadamard256()
+    i = np.arange(256)
+    closed = np.array([[(-1.0) ** _popcount(a & b) / 16.0 for b in i] for a in i])
+    assert np.array_equal(h, closed)
+
+
+def test_h_symmetric_orthonormal_exact():
+    # [P1]: "H is symmetric with HH = I"; divided by sqrt(256) = 16.
+    h = O.hadamard256()
+    assert np.array_equal(h, h.T)
+    assert np.array_equal(h @ h, np.eye(256))
+    assert set(np.unique(np.abs(h))) == {1.0 / 16.0}
+
+
+def test_h_kron_h16():
+    h16 = scipy.linalg.hadamard(16)
+    assert np.array_equal(O.hadamard256_pm1(), np.kron(h16, h16))
+
+
+# -------------------------------------------------------------------- rotation
+
+def _fwht_textbook(v):
+    """In-place iterative Walsh-Hadamard butterflies over the last axis (256)."""
+    v = np.array(v, dtype=np.float64, copy=True)
+    h = 1
+    while h < v.shape[-1]:
+        for i in range(0, v.shape[-1], 2 * h):
+            a = v[..., i:i + h].copy()
+            b = v[..., i + h:i + 2 * h].copy()
+            v[..., i:i + h] = a + b
+            v[..., i + h:i + 2 * h] = a - b
+        h *= 2
+    return v / 16.0
+
+
+def test_rotation_equals_textbook_fwht_per_group():
+    rng = np.random.default_rng(1)
+    x = rng.normal(0, 3, (5, 1024)).astype(np.float16)
+    got = O.rotate_activations_exact(x)
+    want = np.concatenate([_fwht_textbook(x[:, g * 256:(g + 1) * 256].astype(np.float64))
+                           for g in range(4)], axis=1)
+    assert np.array_equal(got, want)          # both exact for fp16 inputs
+
+
+def test_rotation_one_hot_gives_row_of_h_in_its_group():
+    h = O.hadamard256()
+    for g, i in ((0, 0), (0, 77), (2, 255), (3, 5)):
+        x = np.zeros((1, 1024), np.float16)
+        x[0, 256 * g + i] = 1.0
+        r = O.rotate_activations_exact(x)[0]
+        assert np.array_equal(r[256 * g:256 * (g + 1)], h[i])
+        others = np.delete(r, np.s_[256 * g:256 * (g + 1)])
+        assert not others.any()
+
+
+def test_rotation_identity_e2():
+    # [P1]: X_rot W_rot^T = (XH)(WH^T)^T = X H H W^T = X W^T.
+    rng = np.random.default_rng(2)
+    x = rng.normal(0, 1, (16, 512))
+    w = rng.normal(0, 0.02, (24, 512))
+    lhs = O.rotate_f64(x) @ O.rotate_f64(w).T
+    rhs = x @ w.T
+    assert np.linalg.norm(lhs - rhs) <= 1e-13 * np.linalg.norm(rhs)
+    # A wrong grouping (rotating across 512 with a mismatched layout) breaks it.
+    xs = x.copy()
+    xs[:, :256], xs[:, 256:] = x[:, 256:], x[:, :256]
+    bad = O.rotate_f64(xs) @ O.rotate_f64(w).T
+    assert np.linalg.norm(bad - rhs) > 0.1 * np.linalg.norm(rhs)
+
+
+def test_activation_rotation_is_exact_for_extreme_fp16():
+    # fp16 extremes: max, min subnormal, mixed signs; compare with Python ints.
+    rng = np.random.default_rng(3)
+    vals = np.array([65504, -65504, 2.0 ** -24, -(2.0 ** -24), 6.1e-5, 1.0, -0.333], np.float16)
+    x = rng.choice(vals, size=(4, 256)).astype(np.float16)
+    x[1] = rng.normal(0, 1000, 256).astype(np.float16)
+    got = O.rotate_activations_exact(x)
+    hp = scipy.linalg.hadamard(256)
+    for r in range(4):
+        ints = [int(Fraction(float(v)) * 2 ** 24) for v in x[r]]
+        for c in range(256):
+            exact = Fraction(sum(int(hp[k, c]) * ints[k] for k in range(256)), 2 ** 24 * 16)
+            assert Fraction(float(got[r, c])) == exact
+
+
+# ----------------------------------------------------------- exact rounding
+
+def _exact_double(d):
+    f = Fraction(float(d))
+    den = f.denominator
+    shift = den.bit_length() - 1
+    assert den == 1 << shift
+    return f.numerator, shift
+
+
+def test_round_scaled_int_matches_ieee_casts():
+    rng = np.random.default_rng(4)
+    samples = list(rng.normal(0, 1, 300) * np.exp2(rng.integers(-160, 140, 300)))
+    samples += list(rng.normal(0, 1, 200) * np.exp2(rng.integers(-30, 18, 200)))
+    # near fp32/fp16 rounding boundaries and halfway cases
+    samples += [1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, 1 + 2.0 ** -24 + 2.0 ** -40,
+                2.0 ** -150, 3 * 2.0 ** -151, 2.0 ** -149 * 1.5, 2.0 ** -149 * 2.5,
+                3.4028235677973366e38, 3.4028235677973366e38 * (1 + 2.0 ** -25),
+                float(np.finfo(np.float32).max) * (1 + 2.0 ** -24),
+                65504.0, 65519.99, 65520.0, 2.0 ** -25, 3 * 2.0 ** -26, 1 + 2.0 ** -11,
+                1 + 3 * 2.0 ** -11, 2049.0, 2051.0]
+    for d in samples:
+        for neg in (1.0, -1.0):
+            t, sh = _exact_double(neg * d)
+            with np.errstate(over="ignore"):
+                want32 = float(np.float32(neg * d))
+                want16 = float(np.float16(neg * d))
+            assert O.round_scaled_int(t, sh, O.F32) == want32, (neg * d)
+            assert O.round_scaled_int(t, sh, O.F16) == want16, (neg * d)
+
+
+def _is_correct_rounding_f32(exact: Fraction, got: np.float32) -> bool:
+    lo = np.nextafter(got, np.float32(-np.inf), dtype=np.float32)
+    hi = np.nextafter(got, np.float32(np.inf), dtype=np.float32)
+    d = abs(Fraction(float(got)) - exact)
+    for nb in (lo, hi):
+        dn = abs(Fraction(float(nb)) - exact)
+        if dn < d:
+            return False
+        if dn == d:  # tie: the even significand wins
+            if np.array([got], np.float32).view(np.uint32)[0] & 1:
+                return False
+    return True
+
+
+# ------------------------------------------------------- weight rotation (R3)
+
+def test_weight_rotation_exact_on_double_rounding_trap():
+    # exact sum 1 + 2^-24 + 2^-80 lies just above an fp32 halfway point; a float64
+    # sum drops 2^-80, lands on the halfway point and ties to even (downwards).
+    w = np.zeros((1, 256), np.float32)
+    w[0, 0], w[0, 1], w[0, 2] = 1.0, 2.0 ** -24, 2.0 ** -80
+    got = O.rotate_weights_f32(w)[0, 0]
+    exact = (Fraction(1) + Fraction(1, 2 ** 24) + Fraction(1, 2 ** 80)) / 16
+    assert _is_correct_rounding_f32(exact, got)
+    assert got == np.float32((1 + 2.0 ** -23) / 16)
+    naive = np.float32((w.astype(np.float64) @ O.hadamard256())[0, 0])
+    assert naive != got                          # the plausible mistake fails
+
+
+def test_weight_rotation_fast_path_equals_exact_path():
+    rng = np.random.default_rng(5)
+    w = rng.normal(0, 0.02, (6, 512)).astype(np.float32)
+    w[2, 7] = 1e-30                           # forces the exact path for that group
+    w[4, 300] = 3e-12
+    fast = O.rotate_weights_f32(w)
+    exact = O.rotate_weights_f32(w, force_exact=True)
+    assert np.array_equal(fast, exact)
+
+
+def test_weight_rotation_correctly_rounded_sampled():
+    rng = np.random.default_rng(6)
+    w = (rng.normal(0, 1, (2, 256)) * np.exp2(rng.integers(-40, 10, (2, 256)))).astype(np.float32)
+    got = O.rotate_weights_f32(w)
+    hp = scipy.linalg.hadamard(256)
+    for r in range(2):
+        fr = [Fraction(float(v)) for v in w[r]]
+        for c in rng.choice(256, 24, replace=False):
+            exact = sum(int(hp[k, c]) * fr[k] for k in range(256)) / 16
+            assert _is_correct_rounding_f32(exact, got[r, c])
+
+
+# ---------------------------------------------------------------- quantisation
+
+def test_tie_rows_round_half_even():
+    g = _golden()["tie_rows"]
+    rows = []
+    for r in g["rows"]:
+        x = np.empty(256, np.float64)
+        x[0::2] = r["x_even_num"] / r["den"]
+        x[1::2] = r["x_odd_num"] / r["den"]
+        assert np.array_equal(x.astype(np.float16).astype(np.float64), x)  # fp16-exact
+        rows.append(x)
+    x16 = np.array(rows).astype(np.float16)
+    q, s = O.quantize_activations(x16)
+    assert np.all(s == np.float32(g["s_X"]))
+    assert list(q[:, 0]) == [r["Q_X_0"] for r in g["rows"]]
+    assert list(q[:, 1]) == [r["Q_X_1"] for r in g["rows"]]
+    assert not q[:, 2:].any()
+    assert list(q[:, 1]) != g["half_away_from_zero_would_give_Q_X_1"]
+    assert list(q[:, 1]) != g["truncation_would_give_Q_X_1"]
+
+
+def test_constant_row():
+    g = _golden()["constant_row"]
+    x16 = np.full((1, 256), g["c"], np.float16)
+    q, s = O.quantize_activations(x16)
+    assert s[0] == _f32_from_bits(g["s_X_bits"])
+    assert q[0, 0] == 127 and not q[0, 1:].any()
+
+
+def test_one_hot_end_to_end_identity():
+    g = _golden()["one_hot"]
+    x16 = np.eye(256, dtype=np.float16)
+    w = np.eye(256, dtype=np.float32)
+    qw, sw = O.quantize_weights(w)
+    y, qx, sx, a = O.linear_w8a8(x16, qw, sw)
+    s_bits = _f32_from_bits(g["s_X_bits"])
+    assert np.all(sx == s_bits) and np.all(sw == s_bits)
+    assert np.array_equal(qx.astype(np.int64), 127 * scipy.linalg.hadamard(256))
+    assert np.array_equal(qw, qx)
+    assert np.array_equal(a, g["A_diag"] * np.eye(256, dtype=np.int64))
+    assert np.array_equal(y, np.eye(256, dtype=np.float16))
+
+
+def test_quantisation_invariants():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_t(3, (40, 1024)) * 3).astype(np.float16)
+    x[5] = 0
+    q, s = O.quantize_activations(x)
+    assert q.min() >= -127 and q.max() <= 127            # -128 never occurs
+    nz = s > 0
+    assert not nz[5] and not q[5].any()                  # zero row: s = 0, Q = 0
+    assert np.all(np.abs(q[nz]).max(axis=1) == 127)      # every nonzero row hits 127
+    qn, sn = O.quantize_activations(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    for p in (-3, 2):                                    # exact power-of-two scaling
+        q2, s2 = O.quantize_activations((x.astype(np.float32) * 2.0 ** p).astype(np.float16))
+        ok = np.isfinite(x.astype(np.float32) * 2.0 ** p).all()
+        assert ok
+        assert np.array_equal(q2, q) and np.array_equal(s2, (s * np.float32(2.0 ** p)))
+
+
+def test_group_support_stays_in_group():
+    x = np.zeros((1, 768), np.float16)
+    x[0, 256:512] = np.linspace(-4, 4, 256).astype(np.float16)
+    r = O.rotate_activations_exact(x)
+    assert not r[0, :256].any() and not r[0, 512:].any()
+
+
+def test_quantisation_close_to_exact_rational_rounding():
+    # fp32 division + half-even rounding agrees with the exact-rational rounding
+    # except where the exact quotient lies within one fp32 ulp of a half-integer.
+    rng = np.random.default_rng(8)
+    v = rng.normal(0, 1, (6, 256)).astype(np.float32)
+    q, s = O.quantize_rows(v)
+    for r in range(6):
+        for k in range(0, 256, 7):
+            ex = Fraction(float(v[r, k])) / Fraction(float(s[r]))
+            fl = math.floor(ex)
+            frac = ex - fl
+            want = fl if frac < Fraction(1, 2) else fl + 1 if frac > Fraction(1, 2) else (fl if fl % 2 == 0 else fl + 1)
+            if q[r, k] != want:
+                assert abs(frac - Fraction(1, 2)) < Fraction(128, 2 ** 23)
+
+
+# ------------------------------------------------------------- integer product
+
+def test_int_gemm_bruteforce_pages_shape():
+    # [P1] "Running int8xint8 in a Metal kernel": M=37, N=80, K=256, 0 mismatches.
+    g = _golden()["int_parity_shape"]
+    rng = np.random.default_rng(9)
+    qx = rng.integers(-127, 128, (g["M"], g["K"]), dtype=np.int8)
+    qw = rng.integers(-127, 128, (g["N"], g["K"]), dtype=np.int8)
+    qx[0] = 127
+    qw[0] = -127
+    want = np.einsum("mk,nk->mn", qx.astype(np.int64), qw.astype(np.int64))
+    got = O.int8_gemm(qx, qw)
+    assert int((got != want).sum()) == g["mismatches"]
+
+
+def test_int_gemm_extreme_k():
+    k = O.K_MAX
+    qx = np.full((1, k), 127, np.int8)
+    qw = np.full((2, k), 127, np.int8)
+    qw[1] = -127
+    a = O.int8_gemm(qx, qw)
+    assert a[0, 0] == 127 * 127 * k and a[0, 1] == -127 * 127 * k
+    assert a[0, 0] < 2 ** 31
+
+
+# ------------------------------------------------------------------- epilogue
+
+def _rt32(fr: Fraction) -> float:
+    t, sh = fr.numerator, 0
+    d = fr.denominator
+    sh = d.bit_length() - 1
+    assert d == 1 << sh
+    return O.round_scaled_int(t, sh, O.F32)
+
+
+def _rt16(fr: Fraction) -> float:
+    d = fr.denominator
+    sh = d.bit_length() - 1
+    return O.round_scaled_int(fr.numerator, sh, O.F16)
+
+
+def test_epilogue_matches_exact_rational_emulation():
+    rng = np.random.default_rng(10)
+    a = rng.integers(-2 ** 30, 2 ** 30, (4, 5))
+    a[0, 0] = 2 ** 24 + 1           # int -> fp32 rounding is exercised
+    a[1, 1] = 0
+    sx = (rng.random(4) * 1e-2).astype(np.float32)
+    sw = (rng.random(5) * 1e-4).astype(np.float32)
+    bias = rng.normal(0, 1, 5).astype(np.float32)
+    for b in (None, bias):
+        y = O.epilogue_w8a8(a, sx, sw, b)
+        for m in range(4):
+            for n in range(5):
+                af = _rt32(Fraction(int(a[m, n])))
+                sc = _rt32(Fraction(float(sx[m])) * Fraction(float(sw[n])))
+                v = _rt32(Fraction(af) * Fraction(sc))
+                if b is not None:
+                    v = _rt32(Fraction(v) + Fraction(float(b[n])))
+                want = _rt16(Fraction(v))
+                assert float(y[m, n]) == want
+
+
+# ------------------------------------------------- weight-only, fp16, quality
+
+def test_f16_cast_of_exact_double_is_single_rounding():
+    # fp16(exact X_rot) must round once; numpy's float64 -> float16 cast is
+    # checked against the exact rounding routine on halfway-adjacent values.
+    vals = [1 + 2.0 ** -11 + 2.0 ** -40, 1 + 2.0 ** -11 - 2.0 ** -40, 1 + 2.0 ** -11,
+            2049.0 + 2.0 ** -30, 0.1, -7.123456789, 65519.0, 2.0 ** -25 + 2.0 ** -50]
+    for d in vals:
+        t, sh = _exact_double(d)
+        assert float(np.float64(d).astype(np.float16)) == O.round_scaled_int(t, sh, O.F16)
+
+
+def test_w8a16_one_hot():
+    x16 = np.eye(256, dtype=np.float16)
+    qw, sw = O.quantize_weights(np.eye(256, dtype=np.float32))
+    y = O.linear_w8a16(x16, qw, sw)
+    assert np.array_equal(y, np.eye(256, dtype=np.float16))
+
+
+def test_w8a16_lora_rotated_form_identity():
+    # [P4] "Design": the rotated down weight meets the rotated activation; since
+    # H is symmetric and orthogonal, (XH)(DH)^T U^T = X D^T U^T.
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 1, (8, 512))
+    d = rng.normal(0, 0.01, (4, 512))
+    u = rng.normal(0, 0.01, (10, 4))
+    a = (O.rotate_f64(x) @ O.rotate_f64(d).T) @ u.T
+    b = (x @ d.T) @ u.T
+    assert np.linalg.norm(a - b) <= 1e-13 * np.linalg.norm(b)
+
+
+def test_w8a16_lora_and_bias_are_added():
+    rng = np.random.default_rng(12)
+    x16 = rng.normal(0, 1, (6, 256)).astype(np.float16)
+    w = rng.normal(0, 0.02, (9, 256)).astype(np.float32)
+    qw, sw = O.quantize_weights(w)
+    d = rng.normal(0, 0.01, (3, 256)).astype(np.float32)
+    u = rng.normal(0, 0.01, (9, 3)).astype(np.float32)
+    bias = rng.normal(0, 1, 9).astype(np.float32)
+    base = O.linear_w8a16(x16, qw, sw).astype(np.float64)
+    full = O.linear_w8a16(x16, qw, sw, bias=bias, lora=(d, u, 2.0)).astype(np.float64)
+    extra = 2.0 * (x16.astype(np.float64) @ d.T.astype(np.float64)) @ u.T.astype(np.float64) + bias
+    assert np.abs(full - base - extra).max() < 4e-3 * (1 + np.abs(full).max())
+
+
+def test_f16_baseline_integer_inputs_exact():
+    rng = np.random.default_rng(13)
+    x = rng.integers(-8, 9, (7, 256))
+    w = rng.integers(-8, 9, (5, 256))
+    y = O.linear_f16(x.astype(np.float16), w.astype(np.float16))
+    assert np.array_equal(y.astype(np.int64), x @ w.T)      # |sums| < 2048: exact in fp16
+
+
+def test_rotation_reduces_quantisation_error_on_outlier_channels():
+    # [P1]: the rotation spreads outliers so that int8 rounding loses less.
+    rng = np.random.default_rng(14)
+    K = 2048
+    x = rng.normal(0, 1, (64, K))
+    x[:, rng.choice(K, K // 100, replace=False)] *= 50
+    x16 = x.astype(np.float16)
+    w = rng.normal(0, 0.02, (128, K)).astype(np.float32)
+    truth = O.linear_true(x16.astype(np.float64), w)
+    qw, sw = O.quantize_weights(w)
+    y_rot = O.linear_w8a8(x16, qw, sw)[0].astype(np.float64)
+    # same int8 scheme without rotation (reference only, computed here)
+    qx_n, sx_n = O.quantize_rows(x16.astype(np.float32))
+    qw_n, sw_n = O.quantize_rows(w)
+    y_plain = (qx_n.astype(np.float64) @ qw_n.astype(np.float64).T) * np.outer(sx_n, sw_n)
+    e_rot = np.linalg.norm(y_rot - truth) / np.linalg.norm(truth)
+    e_plain = np.linalg.norm(y_plain - truth) / np.linalg.norm(truth)
+    assert e_rot < 0.03
+    assert e_plain > 2 * e_rot
+
+
+def test_scale_spans_the_whole_row_not_one_group():
+    # [P1]: s_X[m] = max over all k of the row, not per 256-group (reading R4).
+    rng = np.random.default_rng(15)
+    x = np.concatenate([rng.normal(0, 1, (3, 256)), 0.01 * rng.normal(0, 1, (3, 256))], axis=1)
+    q, s = O.quantize_activations(x.astype(np.float16))
+    assert np.all(np.abs(q[:, :256]).max(axis=1) == 127)
+    assert np.all(np.abs(q[:, 256:]).max(axis=1) <= 3)
