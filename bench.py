@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the INT8ConvRot W8A8 linear on one MI355X.
+
+Workload: the six weight shapes of the quantised model at M = 1024 activation
+rows, each shape repeated for its layer count (168/84/84/56/28/28 = 448
+layers), as in the six-shape table of the page "INT8ConvRot GEMM vs fp16 on
+M1 Max with Metal, MPSMatrix, and MLX (fp16 Wins)".  A step is one W8A8
+forward of all 448 layers (prologue + int8 GEMM + scale epilogue per layer),
+every layer with its own int8 weight buffer, inputs resident in HBM.  The step
+is captured once in a HIP graph and replayed.
+
+Prints one JSON line: TOPS = sum(2 M N K) / step time, plus the roofline of
+the dominant kernel (the int8 GEMM), the CPU-oracle baseline, and the same
+sweep for the weight-only path and two fp16 GEMMs (ours and torch's
+F.linear) for comparison.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-compare", action="store_true", help="skip the W8A16 / fp16 comparison sweeps")
+    return p.parse_args()
+
+
+def timed_graph(graph, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per replay
+
+
+def capture(fn, stream):
+    import torch
+    fn()  # eager once (first-call setup happens outside the capture)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_src):
+    """Measured HBM bytes per launch of the GEMM, valid only for this source."""
+    path = os.path.join(ROOT, "profiles", "gemm_i8_sweep_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shapes, M):
+    """The oracle, untuned, on the host: one full M=1024 W8A8 call per shape,
+    weighted by layer count like the GPU metric."""
+    import numpy as np
+    import torch
+    from oracle import convrot_oracle as O
+    import workload as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    tot_ops, tot_t = 0.0, 0.0
+    per = []
+    for (N, K, L) in shapes:
+        x = wl.make_activations(M, K, seed=0).numpy()
+        qw, sw = O.quantize_weights(wl.make_weights(N, K, seed=0).numpy())  # offline, untimed
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.linear_w8a8(x, qw, sw)
+            ts.append(time.perf_counter() - t0)
+        t = sorted(ts)[1]
+        per.append({"N": N, "K": K, "seconds": round(t, 4)})
+        tot_ops += L * 2.0 * M * N * K
+        tot_t += L * t
+    return {
+        "value": round(tot_ops / tot_t / 1e12, 4), "unit": "TOPS", "cores": int(cores),
+        "kind": "oracle",
+        "sample": "one W8A8 call (rotate, quantise, int GEMM, epilogue) per shape at M=1024, "
+                  "median of 3 timings each, weighted by the 448 layer counts; weight prep untimed",
+        "per_shape": per,
+        "weighted_total_s": round(tot_t, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        log("bench.py: only --gpus 1 is supported (single-GPU build)")
+        sys.exit(2)
+
+    import torch
+    import torch.nn.functional as F
+    import rotation_quantized_int8_amd as cr
+    import workload as wl
+
+    if not torch.cuda.is_available():
+        log("bench.py: no GPU")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = cr.lib()
+    M = wl.M_FIXED
+    shapes = wl.LAYER_SHAPES
+    stream = torch.cuda.Stream(dev)
+
+    # ---------------------------------------------------------------- setup
+    log("setup: inputs and per-layer int8 weights")
+    per_shape = []
+    for (N, K, layers) in shapes:
+        x = wl.make_activations(M, K, seed=0).to(dev)
+        w = wl.make_weights(N, K, seed=0).to(dev)
+        qw, sw = cr.quantize_weights(w)
+        w16 = w.to(torch.float16)
+        del w
+        qws = [qw] + [qw.clone() for _ in range(layers - 1)]   # one weight buffer per layer
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws8 = torch.empty(cr.workspace_bytes(cr.PATH_W8A8, M, N, K), dtype=torch.uint8, device=dev)
+        ws16 = torch.empty(cr.workspace_bytes(cr.PATH_W8A16, M, N, K, wl.LORA_RANK), dtype=torch.uint8, device=dev)
+        down, up = wl.make_lora(N, K, seed=0)
+        per_shape.append(dict(N=N, K=K, layers=layers, x=x, qws=qws, sw=sw, w16=w16, y=y, ws8=ws8,
+                              ws16=ws16, down=down.to(dev), up=up.to(dev),
+                              qx=ws8[:M * K].view(torch.int8).view(M, K),
+                              sx=ws8[(M * K + 255) // 256 * 256:][:4 * M].view(torch.float32)))
+    torch.cuda.synchronize()
+    ops_step = sum(2.0 * M * s["N"] * s["K"] * s["layers"] for s in per_shape)
+
+    f8a8 = L.convrot_linear_w8a8
+    fpro = L.convrot_act_quant
+    fgemm = L.convrot_gemm_i8_f16
+
+    def w8a8_step():
+        h = torch.cuda.current_stream().cuda_stream
+        for s in per_shape:
+            for q in s["qws"]:
+                st = f8a8(s["x"].data_ptr(), M, s["K"], q.data_ptr(), s["sw"].data_ptr(), s["N"], None,
+                          s["y"].data_ptr(), s["ws8"].data_ptr(), s["ws8"].numel(), h)
+                if st:
+                    raise RuntimeError(L.convrot_status_string(st).decode())
+
+    def prologue_step():
+        h = torch.cuda.current_stream().cuda_stream
+        for s in per_shape:
+            for _ in s["qws"]:
+                st = fpro(s["x"].data_ptr(), M, s["K"], s["qx"].data_ptr(), s["sx"].data_ptr(), h)
+                if st:
+                    raise RuntimeError(L.convrot_status_string(st).decode())
+
+    def gemm_step():
+        h = torch.cuda.current_stream().cuda_stream
+        for s in per_shape:
+            for q in s["qws"]:
+                st = fgemm(s["qx"].data_ptr(), s["sx"].data_ptr(), q.data_ptr(), s["sw"].data_ptr(), None,
+                           M, s["N"], s["K"], s["y"].data_ptr(), h)
+                if st:
+                    raise RuntimeError(L.convrot_status_string(st).decode())
+
+    # ------------------------------------------------------------ main metric
+    log("capture + time: W8A8 step (448 layers)")
+    with torch.cuda.stream(stream):
+        g = capture(w8a8_step, stream)
+        # the graph's result must equal an eager call, replay after replay
+        ref = {}
+        for s in per_shape:
+            s["y"].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = [s["y"].clone() for s in per_shape]
+        for _ in range(3):
+            for s in per_shape:
+                s["y"].zero_()
+            w8a8_step()
+            torch.cuda.synchronize()
+            for s, r in zip(per_shape, ref):
+                if not torch.equal(s["y"].view(torch.int16), r.view(torch.int16)):
+                    raise RuntimeError("graph replay differs from the eager result")
+            g.replay()
+            torch.cuda.synchronize()
+        ms_step = timed_graph(g, args.steps, args.warmup, stream)
+        del g
+
+        log("per-kernel timing: prologue-only and GEMM-only graphs")
+        gp = capture(prologue_step, stream)
+        ms_pro = timed_graph(gp, args.steps, args.warmup, stream)
+        del gp
+        gg = capture(gemm_step, stream)
+        ms_gemm = timed_graph(gg, args.steps, args.warmup, stream)
+        del gg
+
+        # per-shape W8A8 (one layer buffer repeated, graph of 20 calls)
+        shape_rows = []
+        for s in per_shape:
+            def one(s=s):
+                h = torch.cuda.current_stream().cuda_stream
+                for q in s["qws"][:20]:
+                    f8a8(s["x"].data_ptr(), M, s["K"], q.data_ptr(), s["sw"].data_ptr(), s["N"], None,
+                         s["y"].data_ptr(), s["ws8"].data_ptr(), s["ws8"].numel(), h)
+            n_calls = min(20, s["layers"])
+            gs = capture(one, stream)
+            t = timed_graph(gs, max(3, args.steps // 2), 2, stream) / n_calls
+            del gs
+            shape_rows.append({"N": s["N"], "K": s["K"], "layers": s["layers"],
+                               "w8a8_ms": round(t, 5),
+                               "w8a8_tops": round(2.0 * M * s["N"] * s["K"] / (t * 1e-3) / 1e12, 1)})
+
+        compare = {}
+        if not args.no_compare:
+            log("comparison sweeps: W8A16+LoRA, own fp16 GEMM, torch F.linear fp16")
+            def w8a16_step():
+                for s in per_shape:
+                    for q in s["qws"]:
+                        cr.linear_w8a16(s["x"], q, s["sw"], None, (s["down"], s["up"], 1.0), workspace=s["ws16"])
+
+            def own_f16_step():
+                h = torch.cuda.current_stream().cuda_stream
+                for s in per_shape:
+                    for _ in s["qws"]:
+                        L.convrot_gemm_f16(s["x"].data_ptr(), s["w16"].data_ptr(), M, s["N"], s["K"],
+                                           s["y"].data_ptr(), h)
+
+            def torch_f16_step():
+                for s in per_shape:
+                    for _ in s["qws"]:
+                        F.linear(s["x"], s["w16"])
+
+            for name, fn in (("w8a16_lora32", w8a16_step), ("fp16_own_mfma", own_f16_step),
+                             ("fp16_torch_linear", torch_f16_step)):
+                gc = capture(fn, stream)
+                t = timed_graph(gc, args.steps, args.warmup, stream)
+                del gc
+                compare[name] = {"ms_per_step": round(t, 4),
+                                 "tops": round(ops_step / (t * 1e-3) / 1e12, 1)}
+
+    n_launch = sum(s["layers"] for s in per_shape)
+    gemm_src = os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "gemm.hip")
+    traffic = load_traffic(gemm_src)
+    achieved = ops_step / (ms_gemm * 1e-3) / 1e12
+    out = {
+        "metric": "ConvRot W8A8 linear TOPS (2MNK/t) at M=1024, 6 shapes; % int8 MFMA peak",
+        "value": round(ops_step / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "INT8ConvRot W8A8 linear, six-shape layer sweep at M=1024: N x K = "
+                        "2048x2048 (168), 256x2048 (84), 6144x256 (84), 2048x1024 (56), "
+                        "8192x2048 (28), 2048x8192 (28); 448 layers, own int8 weights each",
+            "M": M,
+            "layers": n_launch,
+            "ops_per_step": ops_step,
+            "peak_fraction": round(ops_step / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+        },
+        "roofline": {
+            "kernel": "gemm_kernel<kI8toF16> (int8 MFMA GEMM + scale epilogue)",
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s",
+            "unit_note": "int8 operations (2MNK) per second, against the dense int8 MFMA peak",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(ms_gemm * 1e3 / n_launch, 3),
+            "ops_per_launch_avg": ops_step / n_launch,
+        },
+        "stages": {
+            "prologue_ms_per_step": round(ms_pro, 4),
+            "prologue_avg_launch_us": round(ms_pro * 1e3 / n_launch, 3),
+            "gemm_ms_per_step": round(ms_gemm, 4),
+        },
+        "per_shape": shape_rows,
+        "weighted_total_ms": round(sum(r["w8a8_ms"] * r["layers"] for r in shape_rows), 4),
+        "compare": compare,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(shapes, M)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * convrot.h -- C ABI of the INT8ConvRot linear layer for AMD MI355X (gfx950).
+ *
+ * The method is the one defined on the page "INT8ConvRot GEMM vs fp16 on M1
+ * Max with Metal, MPSMatrix, and MLX (fp16 Wins)", section "What changed in
+ * the computation":
+ *
+ *   H      = (H4 (x) H4 (x) H4 (x) H4) / 16, a symmetric 256x256 matrix with
+ *            HH = I, applied to the last dimension in groups of 256;
+ *   weights (once):  W_rot = W H^T, s_W[n] = max_k |W_rot[n,k]| / 127,
+ *                    Q_W = round(W_rot / s_W) clamped to [-128, 127];
+ *   activations (every call): X_rot = X H, s_X[m] = max_k |X_rot[m,k]| / 127,
+ *                    Q_X = round(X_rot / s_X) clamped to [-128, 127];
+ *   A = Q_X Q_W^T accumulated in int32, Y = A (.) s_X s_W^T.
+ *
+ * Arithmetic contract (the pages leave precision open; this library fixes it):
+ *   - H4 is Sylvester's [[1,1],[1,-1]] (x) [[1,1],[1,-1]];
+ *   - W_rot and X_rot are the exact products rounded once to fp32;
+ *   - s = fp32(max|v|) / 127 and Q = round_half_even(v / s), both IEEE fp32
+ *     divisions; an all-zero row gives s = 0 and Q = 0;
+ *   - Y = fp16( fp32(A) * fp32(s_X[m] * s_W[n]) [+ bias[n]] ), round to nearest
+ *     even at every step, no fused multiply-add.
+ * Under this contract Q_W, s_W, Q_X, s_X, A and the W8A8 output Y are fully
+ * determined, and the library returns exactly those bits.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense and row-major: X, Q_X, Q_W, W and lora.down have
+ *     row stride K; Y and A have row stride N; lora.up has row stride rank.
+ *   - Every tensor pointer is a device pointer on the current HIP device and
+ *     must be 16-byte aligned.  The caller owns every buffer; the library
+ *     allocates nothing, frees nothing and keeps no state between calls
+ *     beyond a per-device cache of the device check.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising.  All argument checks run on
+ *     the host before anything is enqueued; on an error nothing is enqueued
+ *     and no output is touched.
+ *   - Sizes are int64_t.  K must be a positive multiple of 256 and at most
+ *     131072 (so 127 * 127 * K < 2^31 and the int32 accumulator cannot
+ *     overflow).  M == 0 or N == 0 is a valid empty call: nothing is launched.
+ *   - Outputs must not overlap inputs or the workspace.
+ *   - Errors are returned as status codes; nothing is printed, thrown or
+ *     aborted.  A non-finite input gives unspecified (but in-bounds) output.
+ *   - Calls are thread-safe; calls that share an output buffer race.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONVROT_ABI_VERSION 1
+#define CONVROT_GROUP 256
+#define CONVROT_K_MAX 131072
+#define CONVROT_LORA_RANK_MAX 64
+
+typedef enum convrot_status {
+  CONVROT_OK = 0,
+  CONVROT_ERR_INVALID_ARG = 1, /* null pointer with nonzero extent, output overlapping an input */
+  CONVROT_ERR_SHAPE = 2,       /* negative size, K % 256 != 0, K > 131072, bad LoRA rank */
+  CONVROT_ERR_ALIGNMENT = 3,   /* a tensor pointer not aligned to 16 bytes */
+  CONVROT_ERR_DEVICE = 4,      /* current device is not gfx950 or cannot be queried */
+  CONVROT_ERR_LAUNCH = 5,      /* a kernel launch reported an error */
+  CONVROT_ERR_WORKSPACE = 6    /* workspace NULL or smaller than convrot_workspace_bytes() */
+} convrot_status;
+
+typedef enum convrot_path {
+  CONVROT_PATH_W8A8 = 0,
+  CONVROT_PATH_W8A16 = 1
+} convrot_path;
+
+/* Unmerged LoRA of the weight-only linear.  Page "[PR #249] Add an mps
+ * backend: weight-only INT8 and W4A8/W6A8 linears for Apple GPUs", sections
+ * "What" and "Design": lora_down [R, K], lora_up [N, R], lora_scale;
+ * Y += scale * (X down^T) up^T. */
+typedef struct convrot_lora {
+  const float* down; /* device fp32 [rank, K] */
+  const float* up;   /* device fp32 [N, rank] */
+  int64_t rank;      /* 1 .. CONVROT_LORA_RANK_MAX */
+  float scale;
+} convrot_lora;
+
+/* Version of this ABI (CONVROT_ABI_VERSION). */
+int convrot_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* convrot_status_string(int status);
+
+/* Offline weight preparation (the weight equation of "What changed in the
+ * computation"): W fp32 [N, K] -> Q_W int8 [N, K] (rotated and quantised,
+ * one scale per output channel) and s_W fp32 [N].  The rotation is computed
+ * exactly in wide fixed point and rounded once to fp32. */
+convrot_status convrot_quantize_weights(const float* W, int64_t N, int64_t K,
+                                        int8_t* Q_W, float* s_W, void* stream);
+
+/* Bytes of workspace that convrot_linear_w8a8 (path = CONVROT_PATH_W8A8) or
+ * convrot_linear_w8a16 (path = CONVROT_PATH_W8A16, lora_rank = 0 without
+ * LoRA) need for these sizes; 0 for an empty problem, (size_t)-1 for invalid
+ * sizes. */
+size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_t lora_rank);
+
+/* The W8A8 ConvRot linear ("What changed in the computation", activation
+ * and product equations): X fp16 [M, K], Q_W int8 [N, K], s_W fp32 [N],
+ * optional bias fp32 [N] (NULL = none) -> Y fp16 [M, N].  Runs the fused
+ * rotate/absmax/quantise prologue (Q_X and s_X go to the workspace) and the
+ * int8 MFMA GEMM with the scale epilogue. */
+convrot_status convrot_linear_w8a8(const void* X, int64_t M, int64_t K,
+                                   const int8_t* Q_W, const float* s_W, int64_t N,
+                                   const float* bias, void* Y,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The weight-only (W8A16) ConvRot linear: the weight-only listing of "What
+ * changed in the computation" (x_rot fp16 [M,K], qweight int8 [N,K], one
+ * scale per output channel), plus an optional unmerged LoRA (NULL = none).
+ * X16 = fp16(X H) (rounded once from the exact product) goes to the
+ * workspace; Y = fp16(s_W[n] * sum_k X16 Q_W + scale * (X down^T) up^T + bias)
+ * with fp32 accumulation on fp16 MFMA, so Y matches the exact value within
+ * accumulation error, not bit for bit. */
+convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K,
+                                    const int8_t* Q_W, const float* s_W, int64_t N,
+                                    const float* bias, const convrot_lora* lora, void* Y,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- stages (exported for parity tests and per-kernel measurement) ---- */
+
+/* Prologue alone: X fp16 [M, K] -> Q_X int8 [M, K], s_X fp32 [M]. */
+convrot_status convrot_act_quant(const void* X, int64_t M, int64_t K,
+                                 int8_t* Q_X, float* s_X, void* stream);
+
+/* Weight-only prologue alone: X fp16 [M, K] -> X16 = fp16(X H) [M, K]. */
+convrot_status convrot_act_rotate_f16(const void* X, int64_t M, int64_t K,
+                                      void* X16, void* stream);
+
+/* Integer product alone: A int32 [M, N] = Q_X Q_W^T.  Inputs are expected in
+ * [-127, 127] as the quantisers produce them (with -128 codes A is exact only
+ * while 128 * 128 * K < 2^31). */
+convrot_status convrot_gemm_i8_i32(const int8_t* Q_X, const int8_t* Q_W,
+                                   int64_t M, int64_t N, int64_t K,
+                                   int32_t* A, void* stream);
+
+/* Integer product with the scale epilogue: Y fp16 [M, N]. */
+convrot_status convrot_gemm_i8_f16(const int8_t* Q_X, const float* s_X,
+                                   const int8_t* Q_W, const float* s_W, const float* bias,
+                                   int64_t M, int64_t N, int64_t K, void* Y, void* stream);
+
+/* fp16 baseline GEMM (the fp16 column of the six-shape table of [P1]):
+ * Y fp16 [M, N] = X fp16 [M, K] . W fp16 [N, K]^T, fp32 accumulation.
+ * K must be a positive multiple of 256 here as well. */
+convrot_status convrot_gemm_f16(const void* X, const void* W,
+                                int64_t M, int64_t N, int64_t K, void* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

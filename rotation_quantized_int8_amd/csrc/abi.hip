@@ -1,0 +1,263 @@
+// C ABI of the INT8ConvRot library: argument checks, workspace layout and
+// the launches on the caller's stream.  Declarations and the full contract
+// are in include/convrot.h.
+
+#include <atomic>
+#include <cstring>
+
+#include "convrot.h"
+#include "launch.hpp"
+
+
+using namespace convrot;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other / error
+std::atomic<int> g_device_state[kMaxDevices];
+
+convrot_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CONVROT_ERR_DEVICE;
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      st = 2;
+    } else {
+      st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? CONVROT_OK : CONVROT_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool k_ok(int64_t K) { return K > 0 && K % kGroup == 0 && K <= kKMax; }
+
+// [a, a + na) and [b, b + nb) overlap?  (null or empty ranges never overlap)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int lora_ld(int64_t rank) { return rank > 0 ? (int)((rank + 31) / 32 * 32) : 0; }
+
+convrot_status launched(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int convrot_abi_version(void) { return CONVROT_ABI_VERSION; }
+
+const char* convrot_status_string(int status) {
+  switch (status) {
+    case CONVROT_OK: return "ok";
+    case CONVROT_ERR_INVALID_ARG: return "invalid argument (null pointer or overlapping output)";
+    case CONVROT_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 256 in 256..131072, or bad LoRA rank)";
+    case CONVROT_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case CONVROT_ERR_DEVICE: return "current HIP device is not gfx950 or cannot be queried";
+    case CONVROT_ERR_LAUNCH: return "kernel launch failed";
+    case CONVROT_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_t lora_rank) {
+  if (M < 0 || N < 0 || K < 0 || lora_rank < 0 || lora_rank > CONVROT_LORA_RANK_MAX) return (size_t)-1;
+  if (M == 0 || N == 0) return 0;
+  if (!k_ok(K)) return (size_t)-1;
+  if (path == CONVROT_PATH_W8A8) return round256((size_t)M * K) + round256((size_t)M * 4);
+  if (path == CONVROT_PATH_W8A16)
+    return round256((size_t)M * K * 2) + round256((size_t)M * lora_ld(lora_rank) * 2);
+  return (size_t)-1;
+}
+
+convrot_status convrot_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* Q_W,
+                                        float* s_W, void* stream) {
+  if (N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!W || !Q_W || !s_W) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(Q_W) || !aligned16(s_W)) return CONVROT_ERR_ALIGNMENT;
+  const size_t wb = (size_t)N * K * 4, qb = (size_t)N * K, sb = (size_t)N * 4;
+  if (overlap(Q_W, qb, W, wb) || overlap(s_W, sb, W, wb) || overlap(Q_W, qb, s_W, sb))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  return launched(launch_quantize_weights(W, N, K, Q_W, s_W, as_stream(stream)));
+}
+
+convrot_status convrot_act_quant(const void* X, int64_t M, int64_t K, int8_t* Q_X, float* s_X,
+                                 void* stream) {
+  if (M < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!X || !Q_X || !s_X) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Q_X) || !aligned16(s_X)) return CONVROT_ERR_ALIGNMENT;
+  const size_t xb = (size_t)M * K * 2, qb = (size_t)M * K, sb = (size_t)M * 4;
+  if (overlap(Q_X, qb, X, xb) || overlap(s_X, sb, X, xb) || overlap(Q_X, qb, s_X, sb))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  return launched(launch_act_quant(X, M, K, Q_X, s_X, as_stream(stream)));
+}
+
+convrot_status convrot_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
+                                      void* stream) {
+  if (M < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!X || !X16) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(X16)) return CONVROT_ERR_ALIGNMENT;
+  if (overlap(X16, (size_t)M * K * 2, X, (size_t)M * K * 2)) return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  return launched(launch_act_rotate_f16(X, M, K, X16, as_stream(stream)));
+}
+
+convrot_status convrot_gemm_i8_i32(const int8_t* Q_X, const int8_t* Q_W, int64_t M, int64_t N,
+                                   int64_t K, int32_t* A, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!Q_X || !Q_W || !A) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(Q_X) || !aligned16(Q_W) || !aligned16(A)) return CONVROT_ERR_ALIGNMENT;
+  const size_t ab = (size_t)M * N * 4;
+  if (overlap(A, ab, Q_X, (size_t)M * K) || overlap(A, ab, Q_W, (size_t)N * K))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  GemmArgs g{};
+  g.X = Q_X; g.W = Q_W; g.out = A; g.M = M; g.N = N; g.K = K;
+  return launched(launch_gemm<GemmMode::kI8toI32>(g, as_stream(stream)));
+}
+
+static convrot_status check_gemm_i8_f16(const int8_t* Q_X, const float* s_X, const int8_t* Q_W,
+                                        const float* s_W, const float* bias, int64_t M, int64_t N,
+                                        int64_t K, const void* Y) {
+  if (!Q_X || !s_X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(Q_X) || !aligned16(s_X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
+      (bias && !aligned16(bias)))
+    return CONVROT_ERR_ALIGNMENT;
+  const size_t yb = (size_t)M * N * 2;
+  if (overlap(Y, yb, Q_X, (size_t)M * K) || overlap(Y, yb, s_X, (size_t)M * 4) ||
+      overlap(Y, yb, Q_W, (size_t)N * K) || overlap(Y, yb, s_W, (size_t)N * 4) ||
+      overlap(Y, yb, bias, bias ? (size_t)N * 4 : 0))
+    return CONVROT_ERR_INVALID_ARG;
+  return CONVROT_OK;
+}
+
+convrot_status convrot_gemm_i8_f16(const int8_t* Q_X, const float* s_X, const int8_t* Q_W,
+                                   const float* s_W, const float* bias, int64_t M, int64_t N,
+                                   int64_t K, void* Y, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (convrot_status st = check_gemm_i8_f16(Q_X, s_X, Q_W, s_W, bias, M, N, K, Y)) return st;
+  if (convrot_status st = check_device()) return st;
+  GemmArgs g{};
+  g.X = Q_X; g.W = Q_W; g.sX = s_X; g.sW = s_W; g.bias = bias; g.out = Y;
+  g.M = M; g.N = N; g.K = K;
+  return launched(launch_gemm<GemmMode::kI8toF16>(g, as_stream(stream)));
+}
+
+convrot_status convrot_gemm_f16(const void* X, const void* W, int64_t M, int64_t N, int64_t K,
+                                void* Y, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!X || !W || !Y) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return CONVROT_ERR_ALIGNMENT;
+  const size_t yb = (size_t)M * N * 2;
+  if (overlap(Y, yb, X, (size_t)M * K * 2) || overlap(Y, yb, W, (size_t)N * K * 2))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  GemmArgs g{};
+  g.X = X; g.W = W; g.out = Y; g.M = M; g.N = N; g.K = K;
+  return launched(launch_gemm<GemmMode::kF16>(g, as_stream(stream)));
+}
+
+convrot_status convrot_linear_w8a8(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
+                                   const float* s_W, int64_t N, const float* bias, void* Y,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
+      (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
+    return CONVROT_ERR_ALIGNMENT;
+  const size_t need = convrot_workspace_bytes(CONVROT_PATH_W8A8, M, N, K, 0);
+  if (!workspace || workspace_bytes < need) return CONVROT_ERR_WORKSPACE;
+  const size_t yb = (size_t)M * N * 2;
+  if (overlap(Y, yb, X, (size_t)M * K * 2) || overlap(Y, yb, Q_W, (size_t)N * K) ||
+      overlap(Y, yb, s_W, (size_t)N * 4) || overlap(Y, yb, bias, bias ? (size_t)N * 4 : 0) ||
+      overlap(Y, yb, workspace, need) || overlap(workspace, need, X, (size_t)M * K * 2) ||
+      overlap(workspace, need, Q_W, (size_t)N * K) || overlap(workspace, need, s_W, (size_t)N * 4) ||
+      overlap(workspace, need, bias, bias ? (size_t)N * 4 : 0))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  int8_t* QX = reinterpret_cast<int8_t*>(workspace);
+  float* sX = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + round256((size_t)M * K));
+  hipStream_t s = as_stream(stream);
+  if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s))) return st;
+  GemmArgs g{};
+  g.X = QX; g.W = Q_W; g.sX = sX; g.sW = s_W; g.bias = bias; g.out = Y;
+  g.M = M; g.N = N; g.K = K;
+  return launched(launch_gemm<GemmMode::kI8toF16>(g, s));
+}
+
+convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
+                                    const float* s_W, int64_t N, const float* bias,
+                                    const convrot_lora* lora, void* Y, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  const int64_t rank = lora ? lora->rank : 0;
+  if (lora && (rank < 1 || rank > CONVROT_LORA_RANK_MAX)) return CONVROT_ERR_SHAPE;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
+  if (lora && (!lora->down || !lora->up)) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
+      (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)) ||
+      (lora && (!aligned16(lora->down) || !aligned16(lora->up))))
+    return CONVROT_ERR_ALIGNMENT;
+  const size_t need = convrot_workspace_bytes(CONVROT_PATH_W8A16, M, N, K, rank);
+  if (!workspace || workspace_bytes < need) return CONVROT_ERR_WORKSPACE;
+  const size_t yb = (size_t)M * N * 2;
+  const size_t db = lora ? (size_t)rank * K * 4 : 0, ub = lora ? (size_t)N * rank * 4 : 0;
+  const void* dp = lora ? lora->down : nullptr;
+  const void* up = lora ? lora->up : nullptr;
+  if (overlap(Y, yb, X, (size_t)M * K * 2) || overlap(Y, yb, Q_W, (size_t)N * K) ||
+      overlap(Y, yb, s_W, (size_t)N * 4) || overlap(Y, yb, bias, bias ? (size_t)N * 4 : 0) ||
+      overlap(Y, yb, workspace, need) || overlap(Y, yb, dp, db) || overlap(Y, yb, up, ub) ||
+      overlap(workspace, need, X, (size_t)M * K * 2) || overlap(workspace, need, Q_W, (size_t)N * K) ||
+      overlap(workspace, need, s_W, (size_t)N * 4) ||
+      overlap(workspace, need, bias, bias ? (size_t)N * 4 : 0) || overlap(workspace, need, dp, db) ||
+      overlap(workspace, need, up, ub))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  hipStream_t s = as_stream(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  void* X16 = ws;
+  __half* T = reinterpret_cast<__half*>(ws + round256((size_t)M * K * 2));
+  const int t_ld = lora_ld(rank);
+  if (convrot_status st = launched(launch_act_rotate_f16(X, M, K, X16, s))) return st;
+  if (lora) {
+    if (convrot_status st = launched(launch_lora_down(X, lora->down, M, K, (int)rank, t_ld, T, s)))
+      return st;
+  }
+  GemmArgs g{};
+  g.X = X16; g.W = Q_W; g.sW = s_W; g.bias = bias; g.out = Y;
+  g.T = lora ? T : nullptr; g.U = lora ? lora->up : nullptr;
+  g.lora_scale = lora ? lora->scale : 0.0f; g.rank = (int)rank; g.t_ld = t_ld;
+  g.M = M; g.N = N; g.K = K;
+  return launched(launch_gemm<GemmMode::kW8A16>(g, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Shared device helpers of the INT8ConvRot HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace convrot {
+
+constexpr int kGroup = 256;          // rotation group along K
+constexpr int kKMax = 131072;        // 127 * 127 * K < 2^31
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+// Orders LDS traffic between the lanes of one wavefront (no workgroup barrier):
+// earlier LDS writes of the wave are visible to its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// fp64 -> fp16 with a single round-to-nearest-even.  The fp32 intermediate is
+// taken with round-to-odd (truncate, then force the last bit when inexact):
+// 24 >= 11 + 2 significand bits make the second rounding exact in effect.
+__device__ __forceinline__ __half f64_to_f16_rn(double d) {
+  float f = (float)d;
+  double back = (double)f;
+  if (back != d) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs(back) > fabs(d)) u -= 1u;   // step one ulp toward zero
+    u |= 1u;                             // sticky bit: round-to-odd
+    f = __uint_as_float(u);
+  }
+  return __float2half_rn(f);
+}
+
+__device__ __forceinline__ float warp_max16(float v) {
+  // max over the 16 lanes of an aligned 16-lane segment
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max64(float v) {
+  v = warp_max16(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+}  // namespace convrot

@@ -1,0 +1,37 @@
+// Host-side launchers of the INT8ConvRot kernels (internal to the library).
+#pragma once
+
+#include "common.hpp"
+
+namespace convrot {
+
+enum class GemmMode { kI8toI32, kI8toF16, kF16, kW8A16 };
+
+struct GemmArgs {
+  const void* X;        // [M, K] int8 (kI8*) or fp16
+  const void* W;        // [N, K] int8 (kI8*, kW8A16) or fp16 (kF16)
+  const float* sX;      // [M]   (kI8toF16)
+  const float* sW;      // [N]   (kI8toF16, kW8A16)
+  const float* bias;    // [N] or null
+  const __half* T;      // [M, t_ld] fp16 LoRA activation (kW8A16, may be null)
+  const float* U;       // [N, rank] fp32 LoRA up (kW8A16, may be null)
+  float lora_scale;
+  int rank;             // LoRA rank (0 = none)
+  int t_ld;             // row stride of T (rank rounded up to 32)
+  void* out;            // [M, N] int32 or fp16
+  int64_t M, N, K;
+};
+
+template <GemmMode MODE>
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* QW, float* sW,
+                                   hipStream_t stream);
+hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
+                            hipStream_t stream);
+hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
+                                 hipStream_t stream);
+hipError_t launch_lora_down(const void* X, const float* D, int64_t M, int64_t K, int rank,
+                            int t_ld, void* T, hipStream_t stream);
+
+}  // namespace convrot

@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+that include/convrot.h declares, and rejects bad arguments before touching a
+GPU (every call here returns from the host-side checks; no kernel runs)."""
+
+import ctypes
+import os
+
+import pytest
+
+import rotation_quantized_int8_amd as cr
+from rotation_quantized_int8_amd import build as crbuild
+
+OK, INVALID, SHAPE, ALIGN, DEVICE, LAUNCH, WORKSPACE = range(7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(cr.LIB_PATH):
+        crbuild.build()
+    return cr.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = cr.header_functions()
+    assert len(declared) == 11
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(cr._SIGNATURES)
+
+
+def test_version_and_status_strings(L):
+    assert L.convrot_abi_version() == 1
+    for s in range(7):
+        assert L.convrot_status_string(s)
+    assert b"unknown" in L.convrot_status_string(99)
+
+
+def test_workspace_bytes(L):
+    assert L.convrot_workspace_bytes(0, 1024, 2048, 2048, 0) == 1024 * 2048 + 4096
+    assert L.convrot_workspace_bytes(0, 3, 5, 256, 0) == 768 + 256
+    assert L.convrot_workspace_bytes(1, 4, 8, 256, 0) == 2048
+    assert L.convrot_workspace_bytes(1, 4, 8, 256, 32) == 2048 + 256
+    assert L.convrot_workspace_bytes(0, 0, 5, 256, 0) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert L.convrot_workspace_bytes(0, 4, 4, 255, 0) == bad
+    assert L.convrot_workspace_bytes(0, 4, 4, 131072 + 256, 0) == bad
+    assert L.convrot_workspace_bytes(0, -1, 4, 256, 0) == bad
+    assert L.convrot_workspace_bytes(1, 4, 4, 256, 65) == bad
+    assert L.convrot_workspace_bytes(7, 4, 4, 256, 0) == bad
+
+
+P = 1 << 20          # a fake, 16-byte aligned "device" address: never dereferenced
+Q = 1 << 24
+R = 1 << 28
+S = 1 << 30
+
+
+def test_linear_w8a8_argument_errors(L):
+    f = L.convrot_linear_w8a8
+    ws = L.convrot_workspace_bytes(0, 4, 8, 256, 0)
+    # empty problems succeed without touching anything
+    assert f(None, 0, 256, None, None, 8, None, None, None, 0, None) == OK
+    assert f(None, 4, 256, None, None, 0, None, None, None, 0, None) == OK
+    # shapes
+    assert f(P, 4, 255, Q, R, 8, None, S, S + 4096, ws, None) == SHAPE
+    assert f(P, 4, 0, Q, R, 8, None, S, S + 4096, ws, None) == SHAPE
+    assert f(P, -1, 256, Q, R, 8, None, S, S + 4096, ws, None) == SHAPE
+    assert f(P, 4, 131072 + 256, Q, R, 8, None, S, S + 4096, ws, None) == SHAPE
+    # null pointers
+    assert f(None, 4, 256, Q, R, 8, None, S, S + 4096, ws, None) == INVALID
+    assert f(P, 4, 256, Q, R, 8, None, None, S + 4096, ws, None) == INVALID
+    # alignment
+    assert f(P + 2, 4, 256, Q, R, 8, None, S, S + 4096, ws, None) == ALIGN
+    assert f(P, 4, 256, Q, R, 8, R + 4096 + 4, S, S + 4096, ws, None) == ALIGN
+    # workspace
+    assert f(P, 4, 256, Q, R, 8, None, S, None, ws, None) == WORKSPACE
+    assert f(P, 4, 256, Q, R, 8, None, S, S + 4096, ws - 1, None) == WORKSPACE
+    # output overlapping an input or the workspace
+    assert f(P, 4, 256, Q, R, 8, None, P + 16, S + 4096, ws, None) == INVALID
+    assert f(P, 4, 256, Q, R, 8, None, S, S, ws, None) == INVALID
+    assert f(P, 4, 256, Q, R, 8, None, S, P, ws, None) == INVALID
+
+
+def test_linear_w8a16_argument_errors(L):
+    f = L.convrot_linear_w8a16
+    lora = cr._Lora(P, Q, 0, 1.0)
+    ws = L.convrot_workspace_bytes(1, 4, 8, 256, 0)
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), S, S + 4096, ws, None) == SHAPE
+    lora.rank = 65
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), S, S + 4096, ws, None) == SHAPE
+    lora.rank, lora.down = 4, None
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), S, S + 4096, ws, None) == INVALID
+    lora.down = P + 65536 + 8
+    wsl = L.convrot_workspace_bytes(1, 4, 8, 256, 4)
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), S, S + 4096, wsl, None) == ALIGN
+    assert f(P, 4, 256, Q, R, 8, None, None, S, S + 4096, ws - 16, None) == WORKSPACE
+    assert f(None, 0, 256, None, None, 8, None, None, None, None, 0, None) == OK
+
+
+def test_stage_argument_errors(L):
+    assert L.convrot_act_quant(P, 4, 300, Q, R, None) == SHAPE
+    assert L.convrot_act_quant(P, 4, 256, None, R, None) == INVALID
+    assert L.convrot_act_quant(P, 4, 256, Q + 1, R, None) == ALIGN
+    assert L.convrot_act_quant(P, 4, 256, P + 256, R, None) == INVALID
+    assert L.convrot_act_quant(None, 0, 256, None, None, None) == OK
+    assert L.convrot_act_rotate_f16(P, 4, 256, P, None) == INVALID
+    assert L.convrot_gemm_i8_i32(P, Q, 4, 8, 257, R, None) == SHAPE
+    assert L.convrot_gemm_i8_i32(P, Q, 4, 8, 256, P, None) == INVALID
+    assert L.convrot_gemm_i8_f16(P, Q, R, S, None, 4, 8, 256, None, None) == INVALID
+    assert L.convrot_gemm_f16(P, Q, 4, 8, 256, R + 8, None) == ALIGN
+    assert L.convrot_quantize_weights(P, 8, 256, Q, Q + 16, None) == INVALID
+    assert L.convrot_quantize_weights(P, -8, 256, Q, R, None) == SHAPE
+    assert L.convrot_quantize_weights(None, 0, 256, None, None, None) == OK
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    import torch
+    with pytest.raises((ValueError, TypeError)):
+        cr.linear_w8a8(torch.zeros(4, 256, dtype=torch.float16),
+                       torch.zeros(8, 256, dtype=torch.int8), torch.zeros(8))

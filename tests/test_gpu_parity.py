@@ -1,0 +1,350 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (see the design doc for the derivations):
+  * Q_W, s_W, Q_X, s_X, A and the W8A8 output Y: bit-exact.  The library
+    computes the rotations exactly and takes every rounding decision in the
+    same fp32 operations as the oracle, so the spec allowance of +-1
+    at rounding ties is reported (as 0) rather than used.
+  * W8A16 and the fp16 baseline accumulate in fp32 on the MFMA, so Y is
+    compared per element against the oracle's float64 result with
+      |dY| <= ulp16(Y_ref) + 2^-14 * S_main + 2^-9 * S_lora
+    (S_* = the sums of |terms|), plus relative Frobenius error <= 1e-3.
+Inputs come from workload/ (seeded) and are handed to both sides unchanged.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import rotation_quantized_int8_amd as cr
+import workload as wl
+from oracle import convrot_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cr.lib()  # raises if the library is missing: the GPU path must be native
+    torch.cuda.set_device(0)
+
+
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _qw_oracle_and_gpu(w_cpu):
+    qo, so = O.quantize_weights(w_cpu.numpy())
+    qg, sg = cr.quantize_weights(w_cpu.to(DEV))
+    torch.cuda.synchronize()
+    return qo, so, _np(qg), _np(sg)
+
+
+# --------------------------------------------------------------- weights (a0)
+
+@pytest.mark.parametrize("N,K", [(256, 256), (80, 512), (37, 768), (3, 2048), (5, 8192)])
+def test_weight_quant_bitexact(N, K):
+    _say(f"weight quant N={N} K={K}")
+    w = wl.make_weights(N, K, seed=N + K)
+    qo, so, qg, sg = _qw_oracle_and_gpu(w)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(qg, qo)
+
+
+def test_weight_quant_extreme_values_bitexact():
+    _say("weight quant extremes")
+    rng = np.random.default_rng(5)
+    w = (rng.normal(0, 1, (12, 512)) * np.exp2(rng.integers(-140, 120, (12, 512)))).astype(np.float32)
+    w[0] = 0.0                                           # zero row
+    w[1, :3] = [1.0, 2.0 ** -24, 2.0 ** -80]             # double-rounding trap
+    w[1, 3:] = 0.0
+    w[2] = np.float32(2.0 ** -149) * rng.integers(-5, 6, 512)   # subnormals only
+    w[3, 0], w[3, 1] = np.float32(3e38), np.float32(-3e38)      # near fp32 max
+    wt = torch.from_numpy(w)
+    qo, so, qg, sg = _qw_oracle_and_gpu(wt)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(qg, qo)
+    assert so[0] == 0 and not qg[0].any()
+
+
+@pytest.mark.parametrize("N,K", [(n, k) for (n, k, _) in wl.LAYER_SHAPES])
+def test_weight_quant_bitexact_full_shapes(N, K):
+    _say(f"weight quant full N={N} K={K}")
+    w = wl.make_weights(N, K, seed=1)
+    qo, so, qg, sg = _qw_oracle_and_gpu(w)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    assert int((qg != qo).sum()) == 0
+
+
+# ----------------------------------------------------------- prologue (a1-a3)
+
+def _act_compare(x_cpu):
+    qo, so = O.quantize_activations(x_cpu.numpy())
+    qg, sg = cr.act_quant(x_cpu.to(DEV))
+    qg, sg = _np(qg), _np(sg)
+    s_mis = int((sg.view(np.uint32) != so.view(np.uint32)).sum())
+    q_mis = int((qg != qo).sum())
+    return q_mis, s_mis
+
+
+@pytest.mark.parametrize("M,K,dist", [(64, 256, "normal"), (37, 768, "normal"), (300, 2048, "normal"),
+                                      (33, 4096, "t3"), (5, 8192, "normal"), (3, 12288, "t3"),
+                                      (3, 20480, "normal"), (2, 131072, "t3"), (1, 256, "normal")])
+def test_act_quant_bitexact(M, K, dist):
+    _say(f"act quant M={M} K={K} {dist}")
+    x = wl.make_activations(M, K, seed=M * 7 + K, dist=dist)
+    q_mis, s_mis = _act_compare(x)
+    _say(f"  Q_X mismatches {q_mis} / {M * K}, s_X mismatches {s_mis}")
+    assert s_mis == 0 and q_mis == 0
+
+
+def test_act_quant_special_rows():
+    _say("act quant special rows")
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+    rows = []
+    for r in g["tie_rows"]["rows"]:
+        x = np.empty(512)
+        x[0:256:2] = r["x_even_num"] / r["den"]
+        x[1:256:2] = r["x_odd_num"] / r["den"]
+        x[256:] = 0.0
+        rows.append(x)
+    rows.append(np.zeros(512))                                   # zero row
+    rows.append(np.full(512, 65504.0))                           # fp16 max
+    rows.append(np.full(512, -65504.0))
+    rows.append(np.where(np.arange(512) % 3 == 0, 2.0 ** -24, -(2.0 ** -24)))  # subnormals
+    rows.append(np.concatenate([np.full(256, 0.5), np.zeros(256)]))           # constant group
+    x = torch.from_numpy(np.array(rows).astype(np.float16))
+    qo, so = O.quantize_activations(x.numpy())
+    qg, sg = cr.act_quant(x.to(DEV))
+    qg, sg = _np(qg), _np(sg)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(qg, qo)
+    assert list(qg[:4, 1]) == [r["Q_X_1"] for r in g["tie_rows"]["rows"]]
+    assert sg[4] == 0 and not qg[4].any()
+
+
+def test_act_quant_sampled_rows_large_m():
+    # rows are independent: the oracle runs on a sample of the rows
+    M, K = 16384, 8192
+    _say(f"act quant sampled M={M} K={K}")
+    x = wl.make_activations(M, K, seed=3, dist="t3")
+    qg, sg = cr.act_quant(x.to(DEV))
+    rows = np.random.default_rng(0).choice(M, 48, replace=False)
+    rows = np.concatenate([rows, [0, M - 1]])
+    qo, so = O.quantize_activations(x.numpy()[rows])
+    assert np.array_equal(_np(sg)[rows].view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(_np(qg)[rows], qo)
+
+
+# ------------------------------------------------------- integer GEMM (a4)
+
+@pytest.mark.parametrize("M,N,K", [(37, 80, 256), (1, 8, 256), (300, 200, 768), (129, 130, 512),
+                                   (64, 256, 256), (17, 3, 1024), (256, 256, 131072)])
+def test_gemm_i8_i32_bitexact(M, N, K):
+    _say(f"gemm i8->i32 M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    qx = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    if K == 131072:
+        qx[0] = 127
+        qw[0] = 127
+        qw[1] = -127
+    ao = O.int8_gemm(qx, qw)
+    ag = _np(cr.gemm_i8_i32(torch.from_numpy(qx).to(DEV), torch.from_numpy(qw).to(DEV)))
+    assert int((ag.astype(np.int64) != ao).sum()) == 0
+
+
+@pytest.mark.parametrize("N,K", [(n, k) for (n, k, _) in wl.LAYER_SHAPES])
+def test_gemm_i8_i32_bitexact_full_shapes(N, K):
+    M = wl.M_FIXED
+    _say(f"gemm i8->i32 full M={M} N={N} K={K}")
+    rng = np.random.default_rng(N * 3 + K)
+    qx = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    ao = O.int8_gemm(qx, qw)
+    ag = _np(cr.gemm_i8_i32(torch.from_numpy(qx).to(DEV), torch.from_numpy(qw).to(DEV)))
+    assert int((ag.astype(np.int64) != ao).sum()) == 0
+
+
+# ------------------------------------------------------ scale epilogue (a5)
+
+@pytest.mark.parametrize("M,N,K,with_bias", [(37, 80, 256, False), (300, 203, 768, True),
+                                             (1024, 2048, 2048, True)])
+def test_gemm_i8_f16_bitexact_given_same_inputs(M, N, K, with_bias):
+    _say(f"gemm i8->f16 M={M} N={N} K={K} bias={with_bias}")
+    x = wl.make_activations(M, K, seed=11)
+    w = wl.make_weights(N, K, seed=12)
+    qx, sx = O.quantize_activations(x.numpy())
+    qw, sw = O.quantize_weights(w.numpy())
+    bias = wl.make_bias(N, seed=13).numpy() if with_bias else None
+    yo = O.epilogue_w8a8(O.int8_gemm(qx, qw), sx, sw, bias)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    yg = _np(cr.gemm_i8_f16(t(qx), t(sx), t(qw), t(sw), None if bias is None else t(bias)))
+    assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+
+
+# ------------------------------------------------- end-to-end W8A8 (a1-a5)
+
+def _e_max(yg, yo, sx, sw, K):
+    d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
+    return float((d / (np.outer(sx, sw).astype(np.float64) * K + 1e-300)).max())
+
+
+def _w8a8_case(M, N, K, seed=0, dist="normal", bias=False, rows=None):
+    x = wl.make_activations(M, K, seed=seed, dist=dist)
+    w = wl.make_weights(N, K, seed=seed)
+    b = wl.make_bias(N, seed=seed) if bias else None
+    qw_g, sw_g = cr.quantize_weights(w.to(DEV))
+    yg = _np(cr.linear_w8a8(x.to(DEV), qw_g, sw_g, None if b is None else b.to(DEV)))
+    qw, sw = O.quantize_weights(w.numpy())
+    assert np.array_equal(_np(qw_g), qw) and np.array_equal(_np(sw_g).view(np.uint32), sw.view(np.uint32))
+    xs = x.numpy() if rows is None else x.numpy()[rows]
+    yo, qx, sx, a = O.linear_w8a8(xs, qw, sw, None if b is None else b.numpy())
+    ygs = yg if rows is None else yg[rows]
+    mism = int((ygs.view(np.uint16) != yo.view(np.uint16)).sum())
+    emax = _e_max(ygs, yo, sx, sw, K)
+    truth = O.linear_true(xs.astype(np.float64), w.numpy())
+    if b is not None:
+        truth = truth + b.numpy()[None, :]
+    rel = float(np.linalg.norm(ygs.astype(np.float64) - truth) / np.linalg.norm(truth))
+    _say(f"  Y mismatches {mism} / {ygs.size}, e_max {emax:.3g}, rel. error vs unquantised {rel:.4f}")
+    return mism, emax, rel
+
+
+@pytest.mark.parametrize("M,N,K,bias", [(64, 256, 256, False), (64, 256, 256, True),
+                                        (300, 203, 768, True), (1, 1, 256, False), (5, 4, 512, True)])
+def test_linear_w8a8_end_to_end_bitexact(M, N, K, bias):
+    _say(f"linear w8a8 M={M} N={N} K={K} bias={bias}")
+    mism, emax, rel = _w8a8_case(M, N, K, seed=M + N, bias=bias)
+    assert mism == 0 and emax == 0.0
+
+
+@pytest.mark.parametrize("N,K", [(n, k) for (n, k, _) in wl.LAYER_SHAPES])
+def test_linear_w8a8_end_to_end_full_shapes(N, K):
+    _say(f"linear w8a8 full M=1024 N={N} K={K}")
+    mism, emax, rel = _w8a8_case(wl.M_FIXED, N, K, seed=0)
+    assert mism == 0 and emax == 0.0
+    assert rel < 0.05
+
+
+@pytest.mark.parametrize("M", [1, 16, 128, 4096, 16384])
+@pytest.mark.parametrize("N,K", [(8192, 2048), (2048, 8192)])
+@pytest.mark.parametrize("dist", ["normal", "t3"])
+def test_linear_w8a8_m_sweep(M, N, K, dist):
+    _say(f"linear w8a8 m-sweep M={M} N={N} K={K} {dist}")
+    rows = None
+    if M > 1024:
+        rows = np.unique(np.concatenate([np.random.default_rng(M).choice(M, 64, replace=False), [0, M - 1]]))
+    mism, emax, rel = _w8a8_case(M, N, K, seed=2, dist=dist, rows=rows)
+    assert mism == 0 and emax == 0.0
+
+
+def test_linear_w8a8_empty_1d_and_leading_dims():
+    _say("linear w8a8 empty / 1-D / 3-D")
+    K, N = 512, 40
+    w = wl.make_weights(N, K, seed=3)
+    qw, sw = cr.quantize_weights(w.to(DEV))
+    y0 = cr.linear_w8a8(torch.empty((0, K), dtype=torch.float16, device=DEV), qw, sw)
+    assert tuple(y0.shape) == (0, N)
+    x = wl.make_activations(6, K, seed=4)
+    y_full = _np(cr.linear_w8a8(x.to(DEV), qw, sw))
+    y1 = _np(cr.linear_w8a8(x[2].to(DEV), qw, sw))
+    assert y1.shape == (N,) and np.array_equal(y1.view(np.uint16), y_full[2].view(np.uint16))
+    y3 = _np(cr.linear_w8a8(x.reshape(2, 3, K).to(DEV), qw, sw))
+    assert np.array_equal(y3.reshape(6, N).view(np.uint16), y_full.view(np.uint16))
+    # strided input / storage offset
+    xs = torch.zeros((6, 2 * K), dtype=torch.float16)
+    xs[:, K:] = x
+    y_str = _np(cr.linear_w8a8(xs[:, K:].to(DEV), qw, sw))
+    assert np.array_equal(y_str.view(np.uint16), y_full.view(np.uint16))
+
+
+def test_linear_w8a8_deterministic():
+    _say("linear w8a8 determinism")
+    x = wl.make_activations(256, 2048, seed=9).to(DEV)
+    qw, sw = cr.quantize_weights(wl.make_weights(512, 2048, seed=9).to(DEV))
+    a = cr.linear_w8a8(x, qw, sw)
+    b = cr.linear_w8a8(x, qw, sw)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------------ weight-only W8A16 (a6, a7)
+
+def _ulp16(y):
+    a = np.abs(y.astype(np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return np.exp2(e - 10)
+
+
+def _w8a16_case(M, N, K, rank=0, bias=False, seed=0):
+    x = wl.make_activations(M, K, seed=seed)
+    w = wl.make_weights(N, K, seed=seed)
+    qw, sw = O.quantize_weights(w.numpy())
+    b = wl.make_bias(N, seed=seed) if bias else None
+    lora = None
+    if rank:
+        d, u = wl.make_lora(N, K, rank=rank, seed=seed)
+        lora = (d, u, 1.0)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    yg = _np(cr.linear_w8a16(x.to(DEV), t(qw), t(sw), None if b is None else b.to(DEV),
+                             None if lora is None else (lora[0].to(DEV), lora[1].to(DEV), lora[2])))
+    yo = O.linear_w8a16(x.numpy(), qw, sw, None if b is None else b.numpy(),
+                        None if lora is None else (lora[0].numpy(), lora[1].numpy(), lora[2]))
+    x16r = O.rotate_activations_f16(x.numpy()).astype(np.float64)
+    s_main = (np.abs(x16r) @ np.abs(qw.astype(np.float64)).T) * sw.astype(np.float64)[None, :]
+    s_lora = 0.0
+    if rank:
+        tt = np.abs(x.numpy().astype(np.float64) @ lora[0].numpy().astype(np.float64).T)
+        s_lora = tt @ np.abs(lora[1].numpy().astype(np.float64)).T
+    bound = _ulp16(yo) + 2.0 ** -14 * s_main + 2.0 ** -9 * s_lora
+    d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
+    viol = int((d > bound).sum())
+    rel = float(np.linalg.norm(yg.astype(np.float64) - yo.astype(np.float64)) / np.linalg.norm(yo.astype(np.float64)))
+    _say(f"  violations {viol}, max |dY|/bound {float((d / bound).max()):.3f}, rel. Frobenius {rel:.2e}")
+    return viol, rel
+
+
+def test_act_rotate_f16_bitexact():
+    for M, K in ((64, 256), (37, 768), (3, 20480)):
+        _say(f"rotate f16 M={M} K={K}")
+        x = wl.make_activations(M, K, seed=K)
+        yo = O.rotate_activations_f16(x.numpy())
+        yg = _np(cr.act_rotate_f16(x.to(DEV)))
+        assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K,rank,bias", [(64, 256, 256, 0, False), (64, 256, 256, 32, True),
+                                             (300, 203, 768, 17, True), (1, 8, 512, 64, False),
+                                             (1024, 2048, 2048, 32, False), (1024, 256, 2048, 32, True)])
+def test_linear_w8a16_within_tolerance(M, N, K, rank, bias):
+    _say(f"linear w8a16 M={M} N={N} K={K} rank={rank} bias={bias}")
+    viol, rel = _w8a16_case(M, N, K, rank=rank, bias=bias, seed=M + rank)
+    assert viol == 0 and rel <= 1e-3
+
+
+# ----------------------------------------------------------- fp16 baseline (a8)
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (300, 203, 768), (1024, 2048, 2048)])
+def test_gemm_f16_within_tolerance(M, N, K):
+    _say(f"gemm f16 M={M} N={N} K={K}")
+    x = wl.make_activations(M, K, seed=5)
+    w16 = wl.make_weights(N, K, seed=5).to(torch.float16)
+    yo = O.linear_f16(x.numpy(), w16.numpy())
+    yg = _np(cr.gemm_f16(x.to(DEV), w16.to(DEV)))
+    s = np.abs(x.numpy().astype(np.float64)) @ np.abs(w16.numpy().astype(np.float64)).T
+    bound = _ulp16(yo) + 2.0 ** -14 * s
+    d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
+    assert int((d > bound).sum()) == 0
