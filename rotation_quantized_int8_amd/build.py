@@ -4,7 +4,8 @@
 
 Every HIP source under csrc/ is compiled for gfx950 only.  Floating-point
 contraction is off (the W8A8 epilogue's operation order is part of the
-contract) and packed fp32 instructions are disabled.
+contract), packed fp32 instructions are disabled, and MFMA accumulators are
+kept in VGPRs.
 """
 
 from __future__ import annotations
@@ -31,6 +32,9 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: with AGPR accumulators the register
+    # allocator copies them AGPR<->VGPR around the pipelined loop's transitions
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

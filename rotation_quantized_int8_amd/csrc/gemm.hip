@@ -341,9 +341,18 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
+  (void)mode; (void)M; (void)N; (void)K;
+  return 0;
+}
+
 template <GemmMode MODE>
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-  return launch_tile<MODE, 128, 128>(a, stream);
+  if constexpr (MODE == GemmMode::kW8A16) {
+    return launch_tile<MODE, 128, 128>(a, stream);
+  } else {
+    return launch_gemm_dma_cfg<MODE>(a, choose_gemm_cfg(MODE, a.M, a.N, a.K), stream);
+  }
 }
 
 template hipError_t launch_gemm<GemmMode::kI8toI32>(const GemmArgs&, hipStream_t);

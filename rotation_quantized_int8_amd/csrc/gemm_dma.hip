@@ -1,0 +1,378 @@
+// Pipelined MFMA GEMM for operands that go to LDS unchanged: the int8 W8A8
+// product (A = Q_X Q_W^T, optionally with the scale epilogue) and the fp16
+// baseline.  Page "INT8ConvRot GEMM vs fp16 on M1 Max with Metal, MPSMatrix,
+// and MLX (fp16 Wins)", section "What changed in the computation" (A and Y)
+// and the fp16 column of its six-shape table.
+//
+// Data flow (gfx950).  A workgroup of WAVES_M x WAVES_N wavefronts owns a
+// (64 WAVES_M) x (64 WAVES_N) output tile; each wavefront a 64x64 block of
+// 4x4 MFMA fragments.  K advances in 128-byte slices through a ring of STAGES
+// LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4:
+// 64 lanes x 16 B = one 1 KiB block per instruction, no register staging).
+// Up to STAGES-1 slices are in flight while one is consumed.  Each 128-byte
+// LDS row has its 16-byte chunks XOR-swizzled by (row & 7); the DMA places a
+// lane's chunk at that swizzled slot by choosing which global chunk it fetches.
+//
+// Synchronisation per slice: every wave waits (s_waitcnt vmcnt) until its own
+// loads of that slice have landed, then s_barrier makes everyone's loads
+// visible; the refill of the buffer consumed one iteration earlier is issued
+// right after that barrier, which every wave reaches only after its reads of
+// that buffer have returned (lgkmcnt(0) at the end of each iteration).
+//
+// Tile order is XCD-aware: workgroups are dispatched round-robin over the 8
+// XCDs, so the i-th workgroup on XCD x gets the i-th tile of a contiguous
+// range, ordered with M fastest.  Each XCD then streams a few weight panels
+// through its own L2 once while the (small, reused) activation tile set is
+// shared by all XCDs.
+//
+// Rows past M or N are clamped to the last valid row for the loads (so every
+// load is in bounds) and dropped in the epilogue.
+
+#include <type_traits>
+
+#include "launch.hpp"
+
+namespace convrot {
+namespace {
+
+constexpr int kRow = 128;  // bytes of one K slice per tile row
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRow + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low bits 3:0,
+// high bits 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One direct global->LDS load: 64 lanes x 16 bytes land contiguously at LDS
+// byte offset `lds` (wave-uniform).  Issued as inline assembly so that the
+// compiler does not treat it as a store that every later LDS read must wait
+// for; the kernel orders it with explicit vmcnt waits and barriers instead.
+// M0 holds the LDS base; one wait state separates its write from the load.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds) : "memory", "m0");
+}
+
+// L2 prefetch of one cache line per lane: a 4-byte direct-to-LDS load into a
+// scratch area nobody reads.  It costs no registers and is ordered by vmcnt
+// like the slice loads, so the waits below can count it exactly.
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gptr), "s"(lds) : "memory", "m0");
+}
+
+template <GemmMode MODE, int WAVES_M, int WAVES_N, int FM, int FN, int STAGES, int PF>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+gemm_dma_kernel(GemmArgs p) {
+  constexpr bool kInt = (MODE == GemmMode::kI8toI32 || MODE == GemmMode::kI8toF16);
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int WM = 16 * FM, WN = 16 * FN;     // wave tile (m, n)
+  constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
+  constexpr int NBLK = (BM + BN) / 8;           // 1 KiB DMA blocks per slice
+  constexpr int LPW = NBLK / NW;                // DMA instructions per wave per slice
+  constexpr int STAGE_BYTES = (BM + BN) * kRow;
+  constexpr int kElem = kInt ? 1 : 2;
+  constexpr int RPW = (BM + BN) / NW;           // tile rows per wave for the L2 prefetch
+  constexpr int LPF = PF >= 0 ? (RPW + 63) / 64 : 0;   // prefetch instructions per wave per slice
+  constexpr int kAhead = (STAGES - 2) * (LPF + LPW);   // loads issued after the awaited slice
+  static_assert(NBLK % NW == 0, "blocks must split evenly over waves");
+  static_assert(STAGES >= 3 && kAhead < 64, "pipeline depth");
+
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t T = tiles_m * tiles_n;
+  int64_t t;
+  {
+    const int64_t b = blockIdx.x;
+    const int64_t x = b & 7, i = b >> 3;
+    const int64_t per = T >> 3, rem = T & 7;
+    t = x * per + (x < rem ? x : rem) + i;
+  }
+  const int64_t tile_n = t / tiles_m;
+  const int64_t tile_m = t - tile_n * tiles_m;
+  const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
+  const int64_t ld = K * kElem;                  // row bytes of both operands
+  const int64_t nk = ld / kRow;
+
+  // Epilogue operands are fetched first so that their latency hides behind the
+  // main loop (issued before the first DMA, they also complete before it).
+  const int orow = lane & 15;        // output row within a fragment
+  const int ocol = (lane >> 4) * 4;  // first of 4 output columns within a fragment
+  float sxv[FM], swv[FN][4], bsv[FN][4];
+  if constexpr (MODE == GemmMode::kI8toF16) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t m = m0 + wm * WM + j * 16 + orow;
+      sxv[j] = p.sX[m < M ? m : M - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t n = n0 + wn * WN + i * 16 + ocol + r;
+        const int64_t nc = n < N ? n : N - 1;
+        swv[i][r] = p.sW[nc];
+        bsv[i][r] = p.bias ? p.bias[nc] : 0.0f;
+      }
+  }
+
+  // per-lane DMA sources for this wave's blocks (block j: 8 rows, 1 KiB)
+  const char* src[LPW];
+  {
+    const int rl = lane >> 3;                    // row within the block
+    const int chunk = (lane & 7) ^ rl;           // logical chunk landing at slot lane&7
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int j = wave * LPW + i;
+      int64_t row;
+      const char* base;
+      if (j < BM / 8) {
+        row = m0 + 8 * j + rl;
+        row = row < M ? row : M - 1;
+        base = reinterpret_cast<const char*>(p.X);
+      } else {
+        row = n0 + 8 * (j - BM / 8) + rl;
+        row = row < N ? row : N - 1;
+        base = reinterpret_cast<const char*>(p.W);
+      }
+      src[i] = base + row * ld + chunk * 16;
+    }
+  }
+  // per-lane L2-prefetch sources: one tile row each (this wave's RPW rows)
+  const char* pfs[LPF > 0 ? LPF : 1];
+#pragma unroll
+  for (int q = 0; q < LPF; ++q) {
+    int r = q * 64 + lane;
+    r = wave * RPW + (r < RPW ? r : RPW - 1);
+    int64_t row;
+    const char* base;
+    if (r < BM) {
+      row = m0 + r;
+      row = row < M ? row : M - 1;
+      base = reinterpret_cast<const char*>(p.X);
+    } else {
+      row = n0 + (r - BM);
+      row = row < N ? row : N - 1;
+      base = reinterpret_cast<const char*>(p.W);
+    }
+    pfs[q] = base + row * ld;
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+  const uint32_t pf_dst = __builtin_amdgcn_readfirstlane(lds_base + STAGES * STAGE_BYTES + wave * LPF * 256);
+  auto prefetch = [&](int64_t kt) {
+    if constexpr (LPF > 0) {
+      const int64_t k = kt < nk ? kt : nk - 1;   // clamped so that the load count never varies
+#pragma unroll
+      for (int q = 0; q < LPF; ++q) dma4(pfs[q] + k * kRow, pf_dst + q * 256);
+    }
+  };
+  // Slice kt's loads, preceded by the L2 prefetch of slice kt + PF + STAGES - 1.
+  auto issue = [&](int64_t kt) {
+    prefetch(kt + PF + STAGES - 1);
+    const uint32_t dst = lds_base + (uint32_t)(kt % STAGES) * STAGE_BYTES + wave * LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      dma16(src[i] + kt * kRow, __builtin_amdgcn_readfirstlane(dst + i * 1024));
+  };
+
+  using Acc = typename std::conditional<kInt, v4i, v4f>::type;
+  Acc acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+  const int frow = lane & 15;
+  const int fk = lane >> 4;
+  // Fragments of one 64-byte K step, double-buffered in registers.
+  uint4 fa[2][FN], fb[2][FM];
+  auto load_frags = [&](int buf, int64_t kt, int kk) {
+    const char* xs = smem + (int)(kt % STAGES) * STAGE_BYTES;
+    const char* ws = xs + BM * kRow;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+      fa[buf][i] = *reinterpret_cast<const uint4*>(ws + swz(wn * WN + i * 16 + frow, kk * 4 + fk));
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      fb[buf][j] = *reinterpret_cast<const uint4*>(xs + swz(wm * WM + j * 16 + frow, kk * 4 + fk));
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        if constexpr (kInt) {
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              *reinterpret_cast<const v4i*>(&fa[buf][i]), *reinterpret_cast<const v4i*>(&fb[buf][j]),
+              acc[i][j], 0, 0, 0);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              *reinterpret_cast<const v8h*>(&fa[buf][i]), *reinterpret_cast<const v8h*>(&fb[buf][j]),
+              acc[i][j], 0, 0, 0);
+        }
+      }
+  };
+  auto barrier = [&]() {
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+  };
+
+  // Pipeline.  Slices 0 .. STAGES-2 are requested up front; slice s lives in
+  // buffer s % STAGES.  Before the MFMAs of a slice's second K step run, the
+  // wave already holds its fragments; the next slice's first-step fragments
+  // are read right after the barrier that publishes it, and that barrier is
+  // also where the buffer of the slice just finished gets refilled (every
+  // wave has drained its reads of it: lgkmcnt(0) precedes the barrier).
+  // Every slice's loads go out as one group (prefetch + slice), so the number
+  // of loads issued after a given slice is fixed: kAhead once the pipeline is
+  // full; near the end (fewer groups in flight) the waits fall back to 0.
+  if constexpr (LPF > 0)
+    for (int64_t s = 0; s < PF + STAGES - 1; ++s) prefetch(s);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+  if (nk >= STAGES - 1) wait_vmcnt<kAhead>();
+  else wait_vmcnt<0>();
+  barrier();
+  if (STAGES - 1 < nk) issue(STAGES - 1);
+  load_frags(0, 0, 0);
+
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    load_frags(1, kt, 1);
+    mma(0);
+    if (kt + 1 < nk) {
+      if (kt + STAGES - 1 < nk) wait_vmcnt<kAhead>();
+      else wait_vmcnt<0>();
+      wait_lgkm0();
+      barrier();
+      if (kt + STAGES < nk) issue(kt + STAGES);
+      load_frags(0, kt + 1, 0);
+    }
+    mma(1);
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // The finished tile goes through LDS (the ring is free now) so that global
+  // stores are whole 16-byte chunks of contiguous output rows.
+  using OutT = typename std::conditional<MODE == GemmMode::kI8toI32, int32_t, __half>::type;
+  constexpr int kOut = sizeof(OutT);
+  constexpr int ROWB = BN * kOut + 16;            // staged row bytes (+16: bank offset per row)
+  static_assert(BM * ROWB <= STAGES * STAGE_BYTES, "staging tile must fit in the ring");
+  wait_lgkm0();
+  barrier();                                      // every wave is done reading the ring
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int ml = wm * WM + j * 16 + orow;     // row within the tile
+      const int nl = wn * WN + i * 16 + ocol;     // first of 4 columns within the tile
+      char* d = smem + ml * ROWB + nl * kOut;
+      if constexpr (MODE == GemmMode::kI8toI32) {
+        *reinterpret_cast<v4i*>(d) = acc[i][j];
+      } else {
+        __half h[4];
+        if constexpr (MODE == GemmMode::kI8toF16) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // Y = fp16( fp32(A) * fp32(s_X * s_W) [+ bias] ), no contraction
+            const float sc = __fmul_rn(sxv[j], swv[i][r]);
+            float y = __fmul_rn((float)acc[i][j][r], sc);
+            if (p.bias) y = __fadd_rn(y, bsv[i][r]);
+            h[r] = __float2half_rn(y);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(acc[i][j][r]);
+        }
+        uint2 v;
+        v.x = (uint32_t)__half_as_ushort(h[0]) | ((uint32_t)__half_as_ushort(h[1]) << 16);
+        v.y = (uint32_t)__half_as_ushort(h[2]) | ((uint32_t)__half_as_ushort(h[3]) << 16);
+        *reinterpret_cast<uint2*>(d) = v;
+      }
+    }
+  }
+  barrier();
+  constexpr int CPR = BN * kOut / 16;             // 16-byte chunks per tile row
+  constexpr int NTH = 64 * NW;
+  const bool vec_rows = ((N * kOut) % 16) == 0;   // every output row starts 16-byte aligned
+  char* outb = reinterpret_cast<char*>(p.out);
+#pragma unroll 4
+  for (int c = tid; c < BM * CPR; c += NTH) {
+    const int rl = c / CPR, cc = c - rl * CPR;
+    const int64_t m = m0 + rl;
+    if (m >= M) continue;
+    const int64_t n = n0 + cc * (16 / kOut);
+    const char* sp = smem + rl * ROWB + cc * 16;
+    char* gp = outb + (m * N + n) * kOut;
+    if (vec_rows && n + 16 / kOut <= N) {
+      *reinterpret_cast<uint4*>(gp) = *reinterpret_cast<const uint4*>(sp);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16 / kOut; ++e)
+        if (n + e < N) reinterpret_cast<OutT*>(gp)[e] = reinterpret_cast<const OutT*>(sp)[e];
+    }
+  }
+}
+
+template <GemmMode MODE, int WAM, int WAN, int FM, int FN, int ST, int PF>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
+  constexpr int BM = 16 * FM * WAM, BN = 16 * FN * WAN;
+  constexpr int NW = WAM * WAN;
+  constexpr int LPF = PF >= 0 ? ((BM + BN) / NW + 63) / 64 : 0;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const size_t lds = (size_t)ST * (BM + BN) * kRow + (size_t)NW * LPF * 256;
+  auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST, PF>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)tiles), dim3(64 * WAM * WAN), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Configuration table: id -> (wave grid, fragments per wave, pipeline depth).
+// Output tile = (16 FM WAVES_M) x (16 FN WAVES_N) in (M, N).
+template <GemmMode MODE>
+hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
+  switch (cfg) {
+    case 0: return launch_cfg<MODE, 2, 2, 4, 4, 3, -1>(a, stream);   // 128x128
+    case 1: return launch_cfg<MODE, 2, 2, 4, 4, 4, -1>(a, stream);   // 128x128, 4 stages
+    case 2: return launch_cfg<MODE, 2, 2, 8, 4, 3, -1>(a, stream);   // 256x128
+    case 3: return launch_cfg<MODE, 2, 2, 4, 8, 3, -1>(a, stream);   // 128x256
+    case 4: return launch_cfg<MODE, 2, 1, 4, 4, 4, -1>(a, stream);   // 128x64 (2 waves)
+    case 5: return launch_cfg<MODE, 1, 2, 4, 4, 4, -1>(a, stream);   // 64x128 (2 waves)
+    case 6: return launch_cfg<MODE, 1, 1, 4, 4, 4, -1>(a, stream);   // 64x64 (1 wave)
+    case 7: return launch_cfg<MODE, 2, 2, 2, 4, 4, -1>(a, stream);   // 64x128
+    case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4, -1>(a, stream);   // 128x64
+    case 9: return launch_cfg<MODE, 2, 2, 4, 4, 3, 2>(a, stream);    // 128x128 with L2 prefetch
+    case 10: return launch_cfg<MODE, 2, 2, 8, 4, 3, 2>(a, stream);   // 256x128 with L2 prefetch
+    case 11: return launch_cfg<MODE, 2, 2, 4, 2, 4, 3>(a, stream);   // 128x64 with L2 prefetch
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template hipError_t launch_gemm_dma_cfg<GemmMode::kI8toI32>(const GemmArgs&, int, hipStream_t);
+template hipError_t launch_gemm_dma_cfg<GemmMode::kI8toF16>(const GemmArgs&, int, hipStream_t);
+template hipError_t launch_gemm_dma_cfg<GemmMode::kF16>(const GemmArgs&, int, hipStream_t);
+
+}  // namespace convrot

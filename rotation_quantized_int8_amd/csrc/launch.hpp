@@ -25,6 +25,12 @@ struct GemmArgs {
 template <GemmMode MODE>
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
+// Pipelined direct-to-LDS GEMM (int8 and fp16 modes) with an explicit tile
+// configuration id, and the id the library picks for a problem size.
+template <GemmMode MODE>
+hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream);
+int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K);
+
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* QW, float* sW,
                                    hipStream_t stream);
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
