@@ -45,6 +45,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-compare", action="store_true", help="skip the W8A16 / fp16 comparison sweeps")
+    p.add_argument("--profile-kernels", action="store_true",
+                   help="run one eager W8A8 step plus a calibration copy of known size and exit "
+                        "(the program to run under rocprofv3 --pmc)")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
+                        "of a --profile-kernels run into profiles/gemm_i8_sweep_traffic.json and exit")
     return p.parse_args()
 
 
@@ -80,9 +86,15 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+GEMM_SRC = os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "gemm_dma.hip")
+GEMM_KERNEL = "gemm_dma_kernel"
+COPY_BYTES = 256 << 20          # calibration copy: 256 MiB read + 256 MiB written
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemm_i8_sweep_traffic.json")
+
+
 def load_traffic(kernel_src):
     """Measured HBM bytes per launch of the GEMM, valid only for this source."""
-    path = os.path.join(ROOT, "profiles", "gemm_i8_sweep_traffic.json")
+    path = TRAFFIC_JSON
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -90,6 +102,51 @@ def load_traffic(kernel_src):
     if rec.get("source_sha256_16") != source_hash(kernel_src):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _pmc_rows(path, counter):
+    """(kernel name, value in KiB) per dispatch of one counter from rocprofv3's CSV."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """HBM bytes per GEMM launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the calibration copy."""
+    fetch = _pmc_rows(fetch_csv, "FETCH_SIZE")
+    write = _pmc_rows(write_csv, "WRITE_SIZE")
+
+    def calib(rows, what):
+        # the copy is the largest elementwise dispatch of the profiling run
+        cands = [v for (k, v) in rows if "elementwise" in k.lower() or "copy" in k.lower()]
+        if not cands:
+            raise SystemExit(f"no calibration copy found for {what}")
+        return COPY_BYTES / (max(cands) * 1024.0)
+
+    fr, wr = calib(fetch, "FETCH_SIZE"), calib(write, "WRITE_SIZE")
+    gf = [v for (k, v) in fetch if GEMM_KERNEL in k]
+    gw = [v for (k, v) in write if GEMM_KERNEL in k]
+    if not gf or len(gf) != len(gw):
+        raise SystemExit("GEMM dispatch counts differ between the two runs")
+    per_launch = (sum(gf) * fr + sum(gw) * wr) * 1024.0 / len(gf)
+    rec = {
+        "kernel": GEMM_KERNEL,
+        "source_sha256_16": source_hash(GEMM_SRC),
+        "launches": len(gf),
+        "fetch_kib_per_launch_raw": round(sum(gf) / len(gf), 1),
+        "write_kib_per_launch_raw": round(sum(gw) / len(gw), 1),
+        "copy_calibration": {"bytes": COPY_BYTES, "fetch_factor": round(fr, 4), "write_factor": round(wr, 4)},
+        "hbm_bytes_per_launch": round(per_launch),
+    }
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(shapes, M):
@@ -130,6 +187,9 @@ def cpu_baseline(shapes, M):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
         log("bench.py: only --gpus 1 is supported (single-GPU build)")
@@ -200,6 +260,19 @@ def main():
                            M, s["N"], s["K"], s["y"].data_ptr(), h)
                 if st:
                     raise RuntimeError(L.convrot_status_string(st).decode())
+
+    if args.profile_kernels:
+        log("profile run: one eager W8A8 step, then the calibration copy")
+        w8a8_step()
+        torch.cuda.synchronize()
+        w8a8_step()
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)      # elementwise: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        log("profile run done")
+        return
 
     # ------------------------------------------------------------ main metric
     log("capture + time: W8A8 step (448 layers)")
@@ -278,8 +351,7 @@ def main():
                                  "tops": round(ops_step / (t * 1e-3) / 1e12, 1)}
 
     n_launch = sum(s["layers"] for s in per_shape)
-    gemm_src = os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "gemm.hip")
-    traffic = load_traffic(gemm_src)
+    traffic = load_traffic(GEMM_SRC)
     achieved = ops_step / (ms_gemm * 1e-3) / 1e12
     out = {
         "metric": "ConvRot W8A8 linear TOPS (2MNK/t) at M=1024, 6 shapes; % int8 MFMA peak",
@@ -304,7 +376,7 @@ def main():
             "peak_fraction": round(ops_step / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
         },
         "roofline": {
-            "kernel": "gemm_kernel<kI8toF16> (int8 MFMA GEMM + scale epilogue)",
+            "kernel": "gemm_dma_kernel<kI8toF16, ...> (int8 MFMA GEMM + scale epilogue)",
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": PEAK_INT8_TOPS,

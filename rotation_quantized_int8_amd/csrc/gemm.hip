@@ -341,9 +341,13 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Tile choice for the direct-to-LDS kernel.  256x128 tiles read half the
+// operand bytes per output of 128x64 tiles, which pays once they still give
+// most of the 256 CUs a tile; otherwise 128x64 tiles spread the work wider.
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
-  (void)mode; (void)M; (void)N; (void)K;
-  return 0;
+  (void)mode; (void)K;
+  const int64_t big = ((M + 255) / 256) * ((N + 127) / 128);
+  return big >= 160 ? 2 : 8;
 }
 
 template <GemmMode MODE>

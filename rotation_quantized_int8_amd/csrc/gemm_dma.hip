@@ -254,19 +254,23 @@ gemm_dma_kernel(GemmArgs p) {
   if (STAGES - 1 < nk) issue(STAGES - 1);
   load_frags(0, 0, 0);
 
-  for (int64_t kt = 0; kt < nk; ++kt) {
+  // The last slice is peeled off so that the loop body has a single path into
+  // its second MFMA group: the LDS-read counter then only waits for reads that
+  // group actually consumes, not for the next slice's reads issued before it.
+  for (int64_t kt = 0; kt + 1 < nk; ++kt) {
     load_frags(1, kt, 1);
     mma(0);
-    if (kt + 1 < nk) {
-      if (kt + STAGES - 1 < nk) wait_vmcnt<kAhead>();
-      else wait_vmcnt<0>();
-      wait_lgkm0();
-      barrier();
-      if (kt + STAGES < nk) issue(kt + STAGES);
-      load_frags(0, kt + 1, 0);
-    }
+    if (kt + STAGES - 1 < nk) wait_vmcnt<kAhead>();
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    barrier();
+    if (kt + STAGES < nk) issue(kt + STAGES);
+    load_frags(0, kt + 1, 0);
     mma(1);
   }
+  load_frags(1, nk - 1, 1);
+  mma(0);
+  mma(1);
 
   // ---------------------------------------------------------------- epilogue
   // The finished tile goes through LDS (the ring is free now) so that global
@@ -367,6 +371,9 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 9: return launch_cfg<MODE, 2, 2, 4, 4, 3, 2>(a, stream);    // 128x128 with L2 prefetch
     case 10: return launch_cfg<MODE, 2, 2, 8, 4, 3, 2>(a, stream);   // 256x128 with L2 prefetch
     case 11: return launch_cfg<MODE, 2, 2, 4, 2, 4, 3>(a, stream);   // 128x64 with L2 prefetch
+    case 12: return launch_cfg<MODE, 2, 2, 4, 2, 5, -1>(a, stream);  // 128x64, 5 stages
+    case 13: return launch_cfg<MODE, 2, 2, 4, 2, 6, -1>(a, stream);  // 128x64, 6 stages
+    case 14: return launch_cfg<MODE, 2, 2, 4, 4, 5, -1>(a, stream);  // 128x128, 5 stages
     default: return hipErrorInvalidValue;
   }
 }
