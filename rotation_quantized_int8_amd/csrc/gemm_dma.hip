@@ -5,25 +5,31 @@
 // and the fp16 column of its six-shape table.
 //
 // Data flow (gfx950).  A workgroup of WAVES_M x WAVES_N wavefronts owns a
-// (64 WAVES_M) x (64 WAVES_N) output tile; each wavefront a 64x64 block of
-// 4x4 MFMA fragments.  K advances in 128-byte slices through a ring of STAGES
-// LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4:
-// 64 lanes x 16 B = one 1 KiB block per instruction, no register staging).
-// Up to STAGES-1 slices are in flight while one is consumed.  Each 128-byte
-// LDS row has its 16-byte chunks XOR-swizzled by (row & 7); the DMA places a
-// lane's chunk at that swizzled slot by choosing which global chunk it fetches.
+// (16 FM WAVES_M) x (16 FN WAVES_N) output tile; each wavefront an FM x FN
+// block of 16x16 MFMA fragments.  K advances in 128-byte slices through a
+// ring of STAGES LDS buffers filled by direct global->LDS loads
+// (global_load_lds_dwordx4: 64 lanes x 16 B = one 1 KiB block of 8 rows per
+// instruction, no register staging).  STAGES-1 slices are in flight while one
+// is consumed.  Each 128-byte LDS row has its 16-byte chunks XOR-swizzled by
+// (row & 7), which makes both the fills and the fragment reads conflict-free;
+// the direct load places a lane's chunk at its swizzled slot by choosing
+// which global chunk that lane fetches.
 //
 // Synchronisation per slice: every wave waits (s_waitcnt vmcnt) until its own
-// loads of that slice have landed, then s_barrier makes everyone's loads
-// visible; the refill of the buffer consumed one iteration earlier is issued
-// right after that barrier, which every wave reaches only after its reads of
-// that buffer have returned (lgkmcnt(0) at the end of each iteration).
+// loads of the next slice have landed and its LDS reads are done (lgkmcnt),
+// then s_barrier publishes everyone's loads; the refill of the buffer just
+// consumed is issued right after that barrier.  The direct loads are written
+// as inline assembly so that the compiler does not treat them as LDS stores
+// that every later fragment read must wait for.
+//
+// Epilogue: the scale operands are fetched at kernel entry; the finished tile
+// is converted in registers, staged through the (now idle) LDS ring and
+// written as whole 16-byte chunks of contiguous output rows.
 //
 // Tile order is XCD-aware: workgroups are dispatched round-robin over the 8
 // XCDs, so the i-th workgroup on XCD x gets the i-th tile of a contiguous
 // range, ordered with M fastest.  Each XCD then streams a few weight panels
-// through its own L2 once while the (small, reused) activation tile set is
-// shared by all XCDs.
+// through its own L2 once while the activation tiles are shared.
 //
 // Rows past M or N are clamped to the last valid row for the loads (so every
 // load is in bounds) and dropped in the epilogue.
