@@ -70,6 +70,23 @@ def timed_graph(graph, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per replay
 
 
+def median_sets(graph, sets, stream):
+    """Median over `sets` individually timed replays (ms per replay)."""
+    import torch
+    graph.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(sets):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ts.append(start.elapsed_time(end))
+    return sorted(ts)[len(ts) // 2]
+
+
 def capture(fn, stream):
     import torch
     fn()  # eager once (first-call setup happens outside the capture)
@@ -193,8 +210,8 @@ def main():
         summarize_pmc(*args.summarize_pmc)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
-        log("bench.py: only --gpus 1 is supported (single-GPU build)")
+        print(json.dumps({"error": "single-GPU implementation: --gpus must be 1"}), flush=True)
+        log("bench.py: only --gpus 1 is supported (single-GPU implementation)")
         sys.exit(2)
 
     import torch
@@ -308,21 +325,44 @@ def main():
         ms_gemm = timed_graph(gg, args.steps, args.warmup, stream)
         del gg
 
-        # per-shape W8A8 (one layer buffer repeated, graph of 20 calls)
+        # Per shape, the pages' protocol: 20 back-to-back calls on hot buffers,
+        # timed as 7 sets; median per call.  Graph-captured, so launch cost is
+        # the in-graph dispatch cost, as in the step above.
+        log("per-shape timings (median of 7 sets of 20 calls)")
         shape_rows = []
         for s in per_shape:
-            def one(s=s):
-                h = torch.cuda.current_stream().cuda_stream
-                for q in s["qws"][:20]:
-                    f8a8(s["x"].data_ptr(), M, s["K"], q.data_ptr(), s["sw"].data_ptr(), s["N"], None,
-                         s["y"].data_ptr(), s["ws8"].data_ptr(), s["ws8"].numel(), h)
-            n_calls = min(20, s["layers"])
-            gs = capture(one, stream)
-            t = timed_graph(gs, max(3, args.steps // 2), 2, stream) / n_calls
-            del gs
-            shape_rows.append({"N": s["N"], "K": s["K"], "layers": s["layers"],
-                               "w8a8_ms": round(t, 5),
-                               "w8a8_tops": round(2.0 * M * s["N"] * s["K"] / (t * 1e-3) / 1e12, 1)})
+            N, K = s["N"], s["K"]
+            q, x, y = s["qws"][0], s["x"], s["y"]
+
+            def calls(fn):
+                def run():
+                    h = torch.cuda.current_stream().cuda_stream
+                    for _ in range(20):
+                        fn(h)
+                return run
+
+            legs = {
+                "w8a8": calls(lambda h: f8a8(x.data_ptr(), M, K, q.data_ptr(), s["sw"].data_ptr(), N, None,
+                                             y.data_ptr(), s["ws8"].data_ptr(), s["ws8"].numel(), h)),
+                "prologue": calls(lambda h: fpro(x.data_ptr(), M, K, s["qx"].data_ptr(), s["sx"].data_ptr(), h)),
+                "gemm_i8_f16": calls(lambda h: fgemm(s["qx"].data_ptr(), s["sx"].data_ptr(), q.data_ptr(),
+                                                     s["sw"].data_ptr(), None, M, N, K, y.data_ptr(), h)),
+            }
+            if not args.no_compare:
+                qwt = q.t()
+                legs["fp16_own_mfma"] = calls(lambda h: L.convrot_gemm_f16(x.data_ptr(), s["w16"].data_ptr(),
+                                                                           M, N, K, y.data_ptr(), h))
+                legs["fp16_torch_linear"] = calls(lambda h: F.linear(x, s["w16"]))
+                legs["int8_torch_int_mm"] = calls(lambda h: torch._int_mm(s["qx"], qwt))
+            row = {"N": N, "K": K, "layers": s["layers"]}
+            for name, fn in legs.items():
+                gs = capture(fn, stream)
+                t = median_sets(gs, 7, stream) / 20
+                del gs
+                row[name + "_us"] = round(t * 1e3, 3)
+            row["w8a8_tops"] = round(2.0 * M * N * K / (row["w8a8_us"] * 1e-6) / 1e12, 1)
+            row["gemm_tops"] = round(2.0 * M * N * K / (row["gemm_i8_f16_us"] * 1e-6) / 1e12, 1)
+            shape_rows.append(row)
 
         compare = {}
         if not args.no_compare:
@@ -395,7 +435,7 @@ def main():
             "gemm_ms_per_step": round(ms_gemm, 4),
         },
         "per_shape": shape_rows,
-        "weighted_total_ms": round(sum(r["w8a8_ms"] * r["layers"] for r in shape_rows), 4),
+        "weighted_total_ms": round(sum(r["w8a8_us"] * r["layers"] for r in shape_rows) / 1e3, 4),
         "compare": compare,
     }
     if not args.no_cpu_baseline:

@@ -27,7 +27,7 @@ rotated and kept in fp16 and multiplied by the int8 weights and their
 per-channel scale.  [P4] section "Design" adds the unmerged LoRA
 (lora_down [R, K], lora_up [N, R], lora_scale) to that linear.
 
-Readings where the pages leave a step open (each one is listed in the design doc):
+Readings where the pages leave a step open:
   R1  the 4x4 Hadamard is Sylvester's [[1,1],[1,-1]] (x) [[1,1],[1,-1]];
   R2  "round" is round-half-to-even, and every division is an IEEE fp32 division;
   R3  W_rot and X_rot are the exact products rounded once to fp32; s and Q are

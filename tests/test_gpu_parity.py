@@ -1,10 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Bars (see the design doc for the derivations):
+Bars:
   * Q_W, s_W, Q_X, s_X, A and the W8A8 output Y: bit-exact.  The library
     computes the rotations exactly and takes every rounding decision in the
-    same fp32 operations as the oracle, so the spec allowance of +-1
-    at rounding ties is reported (as 0) rather than used.
+    same fp32 operations as the oracle, so no allowance at rounding ties is
+    needed.
   * W8A16 and the fp16 baseline accumulate in fp32 on the MFMA, so Y is
     compared per element against the oracle's float64 result with
       |dY| <= ulp16(Y_ref) + 2^-14 * S_main + 2^-9 * S_lora
