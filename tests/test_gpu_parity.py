@@ -281,6 +281,71 @@ def test_linear_w8a8_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("M,N,K", [(40, 64, 16384), (7, 48, 65536), (3, 16, 131072)])
+def test_linear_w8a8_long_rows_bitexact(M, N, K):
+    # rows longer than one prologue pass: the transform is recomputed per chunk
+    _say(f"linear w8a8 long rows M={M} N={N} K={K}")
+    mism, emax, rel = _w8a8_case(M, N, K, seed=K % 97)
+    assert mism == 0 and emax == 0.0
+
+
+def test_linear_w8a8_workspace_reuse():
+    # one workspace (filled with garbage first) for calls of different sizes,
+    # back to back: every result bit-exact
+    _say("linear w8a8 workspace reuse")
+    shapes = [(1024, 2048, 2048), (16, 256, 8192), (300, 203, 768), (2048, 8192, 2048), (1, 8, 256)]
+    need = max(cr.workspace_bytes(cr.PATH_W8A8, M, N, K) for (M, N, K) in shapes)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+    for i, (M, N, K) in enumerate(shapes):
+        x = wl.make_activations(M, K, seed=20 + i)
+        w = wl.make_weights(N, K, seed=20 + i)
+        qw, sw = O.quantize_weights(w.numpy())
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+        yg = _np(cr.linear_w8a8(x.to(DEV), t(qw), t(sw), workspace=ws))
+        torch.cuda.synchronize()
+        yo = O.linear_w8a8(x.numpy(), qw, sw)[0]
+        mism = int((yg.view(np.uint16) != yo.view(np.uint16)).sum())
+        _say(f"  M={M} N={N} K={K}: mismatches {mism}")
+        assert mism == 0
+
+
+def test_linear_w8a8_graph_replays_match_eager():
+    # a captured graph of W8A8 calls, replayed with eager work in between
+    _say("linear w8a8 graph replay vs eager")
+    M, N, K = 512, 2048, 2048
+    x = wl.make_activations(M, K, seed=31).to(DEV)
+    qw, sw = cr.quantize_weights(wl.make_weights(N, K, seed=31).to(DEV))
+    ws = torch.empty(cr.workspace_bytes(cr.PATH_W8A8, M, N, K), dtype=torch.uint8, device=DEV)
+    ref = cr.linear_w8a8(x, qw, sw, workspace=ws).clone()
+    ys = [torch.empty((M, N), dtype=torch.float16, device=DEV) for _ in range(3)]
+    stream = torch.cuda.Stream()
+    L = cr.lib()
+    def calls():
+        h = torch.cuda.current_stream().cuda_stream
+        for y in ys:
+            st = L.convrot_linear_w8a8(x.data_ptr(), M, K, qw.data_ptr(), sw.data_ptr(), N, None,
+                                       y.data_ptr(), ws.data_ptr(), ws.numel(), h)
+            assert st == 0
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for y in ys:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y in ys:
+            assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        e = cr.linear_w8a8(x, qw, sw, workspace=ws)   # eager call between replays
+        torch.cuda.synchronize()
+        assert torch.equal(e.view(torch.int16), ref.view(torch.int16))
+    _say("  4 replays x 3 calls equal to the eager result")
+
+
 # ------------------------------------------------ weight-only W8A16 (a6, a7)
 
 def _ulp16(y):
