@@ -1,19 +1,26 @@
-// Pipelined MFMA GEMM for operands that go to LDS unchanged: the int8 W8A8
-// product (A = Q_X Q_W^T, optionally with the scale epilogue) and the fp16
-// baseline.  Page "INT8ConvRot GEMM vs fp16 on M1 Max with Metal, MPSMatrix,
-// and MLX (fp16 Wins)", section "What changed in the computation" (A and Y)
-// and the fp16 column of its six-shape table.
+// Pipelined MFMA GEMMs whose operands go to LDS by direct global->LDS loads:
+// the int8 W8A8 product (A = Q_X Q_W^T, optionally with the scale epilogue),
+// the weight-only product (fp16 activations times int8 weights; s_W, bias and
+// the unmerged LoRA in the epilogue) and the fp16 baseline.  Page "INT8ConvRot
+// GEMM vs fp16 on M1 Max with Metal, MPSMatrix, and MLX (fp16 Wins)", section
+// "What changed in the computation" (A, Y and the weight-only listing) and
+// the fp16 column of its six-shape table; page "[PR #249] Add an mps backend
+// ...", sections "What" and "Design" (the LoRA term).
 //
 // Data flow (gfx950).  A workgroup of WAVES_M x WAVES_N wavefronts owns a
 // (16 FM WAVES_M) x (16 FN WAVES_N) output tile; each wavefront an FM x FN
-// block of 16x16 MFMA fragments.  K advances in 128-byte slices through a
-// ring of STAGES LDS buffers filled by direct global->LDS loads
-// (global_load_lds_dwordx4: 64 lanes x 16 B = one 1 KiB block of 8 rows per
-// instruction, no register staging).  STAGES-1 slices are in flight while one
-// is consumed.  Each 128-byte LDS row has its 16-byte chunks XOR-swizzled by
-// (row & 7), which makes both the fills and the fragment reads conflict-free;
-// the direct load places a lane's chunk at its swizzled slot by choosing
-// which global chunk that lane fetches.
+// block of 16x16 MFMA fragments.  K advances in slices of 128 activation
+// bytes per row (128 int8 or 64 fp16 values) through a ring of STAGES LDS
+// buffers filled by direct global->LDS loads (global_load_lds_dwordx4:
+// 64 lanes x 16 B = one 1 KiB block per instruction, no register staging).
+// STAGES-1 slices are in flight while one is consumed.  128-byte LDS rows
+// have their 16-byte chunks XOR-swizzled by (row & 7); the weight-only
+// mode's int8 weight rows are 64 bytes per slice (16 rows per block) with
+// their chunks swizzled by ((row >> 2) & 3).  Both make the fills and the
+// fragment reads conflict-free; a direct load places a lane's chunk at its
+// swizzled slot by choosing which global chunk that lane fetches.  In the
+// weight-only mode each lane widens its 8-byte weight fragment to fp16 in
+// registers (exact for int8) before the fp16 MFMA.
 //
 // Synchronisation per slice: every wave waits (s_waitcnt vmcnt) until its own
 // loads of the next slice have landed and its LDS reads are done (lgkmcnt),
@@ -22,8 +29,8 @@
 // as inline assembly so that the compiler does not treat them as LDS stores
 // that every later fragment read must wait for.
 //
-// Epilogue: the scale operands are fetched at kernel entry; the finished tile
-// is converted in registers, staged through the (now idle) LDS ring and
+// Epilogue: scale and bias operands are fetched at kernel entry; the finished
+// tile is converted in registers, staged through the (now idle) LDS ring and
 // written as whole 16-byte chunks of contiguous output rows.
 //
 // Tile order is XCD-aware: workgroups are dispatched round-robin over the 8
@@ -41,9 +48,12 @@
 namespace convrot {
 namespace {
 
-constexpr int kRow = 128;  // bytes of one K slice per tile row
+constexpr int kRowX = 128;  // activation bytes of one K slice per row
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRow + ((chunk ^ (row & 7)) << 4); }
+// 128-byte rows: chunk c of row r at slot c ^ (r & 7)
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// 64-byte rows (weight-only int8 weights): chunk c of row r at slot c ^ ((r >> 2) & 3)
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -68,29 +78,49 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
                :: "v"(gptr), "s"(lds) : "memory", "m0");
 }
 
-// L2 prefetch of one cache line per lane: a 4-byte direct-to-LDS load into a
-// scratch area nobody reads.  It costs no registers and is ordered by vmcnt
-// like the slice loads, so the waits below can count it exactly.
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(gptr), "s"(lds) : "memory", "m0");
+// 8 int8 values (two dwords) -> 8 fp16, exactly: with the sign bit flipped a
+// byte u = b + 128 sits under the fp16 pattern 0x64 (1024 + u), and
+// subtracting 1152 leaves b.  All three steps are exact in fp16.
+__device__ __forceinline__ v8h widen_i8x8(uint2 w) {
+  typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+  const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
+  uint32_t h[4];
+  // v_perm_b32 selector bytes 0-3 pick from the second operand, 4-7 from the first
+  h[0] = __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u);  // bytes 0, 1
+  h[1] = __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u);  // bytes 2, 3
+  h[2] = __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u);
+  h[3] = __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u);
+  v8h r;
+  const v2h bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v2h v = *reinterpret_cast<const v2h*>(&h[q]) - bias;
+    r[2 * q] = v[0];
+    r[2 * q + 1] = v[1];
+  }
+  return r;
 }
 
-template <GemmMode MODE, int WAVES_M, int WAVES_N, int FM, int FN, int STAGES, int PF>
+template <GemmMode MODE, int WAVES_M, int WAVES_N, int FM, int FN, int STAGES>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_dma_kernel(GemmArgs p) {
   constexpr bool kInt = (MODE == GemmMode::kI8toI32 || MODE == GemmMode::kI8toF16);
+  constexpr bool kW16 = (MODE == GemmMode::kW8A16);
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = 16 * FM, WN = 16 * FN;     // wave tile (m, n)
   constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
-  constexpr int NBLK = (BM + BN) / 8;           // 1 KiB DMA blocks per slice
-  constexpr int LPW = NBLK / NW;                // DMA instructions per wave per slice
-  constexpr int STAGE_BYTES = (BM + BN) * kRow;
-  constexpr int kElem = kInt ? 1 : 2;
-  constexpr int RPW = (BM + BN) / NW;           // tile rows per wave for the L2 prefetch
-  constexpr int LPF = PF >= 0 ? (RPW + 63) / 64 : 0;   // prefetch instructions per wave per slice
-  constexpr int kAhead = (STAGES - 2) * (LPF + LPW);   // loads issued after the awaited slice
+  constexpr int kRowW = kW16 ? 64 : 128;        // weight bytes of one K slice per row
+  constexpr int WROWS = 1024 / kRowW;           // weight rows per 1 KiB block
+  constexpr int XBLK = BM / 8;                  // activation blocks per slice
+  constexpr int NBLK = XBLK + BN / WROWS;       // 1 KiB direct loads per slice
+  constexpr int LPW = NBLK / NW;                // per wave per slice
+  constexpr int XBYTES = BM * kRowX;
+  constexpr int STAGE_BYTES = XBYTES + BN * kRowW;
+  constexpr int kElemX = kInt ? 1 : 2;
+  constexpr int kElemW = (MODE == GemmMode::kF16) ? 2 : 1;
+  constexpr int kAhead = (STAGES - 2) * LPW;    // loads issued after the awaited slice
   static_assert(NBLK % NW == 0, "blocks must split evenly over waves");
+  static_assert(BN % WROWS == 0, "whole weight blocks");
   static_assert(STAGES >= 3 && kAhead < 64, "pipeline depth");
 
   extern __shared__ __align__(16) char smem[];
@@ -113,11 +143,12 @@ gemm_dma_kernel(GemmArgs p) {
   const int64_t tile_n = t / tiles_m;
   const int64_t tile_m = t - tile_n * tiles_m;
   const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
-  const int64_t ld = K * kElem;                  // row bytes of both operands
-  const int64_t nk = ld / kRow;
+  const int64_t ldx = K * kElemX;                // row bytes of the activations
+  const int64_t ldw = K * kElemW;                // row bytes of the weights
+  const int64_t nk = ldx / kRowX;
 
   // Epilogue operands are fetched first so that their latency hides behind the
-  // main loop (issued before the first DMA, they also complete before it).
+  // main loop (issued before the first direct load, they also complete first).
   const int orow = lane & 15;        // output row within a fragment
   const int ocol = (lane >> 4) * 4;  // first of 4 output columns within a fragment
   float sxv[FM], swv[FN][4], bsv[FN][4];
@@ -127,6 +158,8 @@ gemm_dma_kernel(GemmArgs p) {
       const int64_t m = m0 + wm * WM + j * 16 + orow;
       sxv[j] = p.sX[m < M ? m : M - 1];
     }
+  }
+  if constexpr (MODE == GemmMode::kI8toF16 || kW16) {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -138,63 +171,41 @@ gemm_dma_kernel(GemmArgs p) {
       }
   }
 
-  // per-lane DMA sources for this wave's blocks (block j: 8 rows, 1 KiB)
+  // per-lane direct-load sources for this wave's blocks
   const char* src[LPW];
-  {
-    const int rl = lane >> 3;                    // row within the block
-    const int chunk = (lane & 7) ^ rl;           // logical chunk landing at slot lane&7
+  int sstep[LPW];                                // bytes per slice of that source
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int j = wave * LPW + i;
-      int64_t row;
-      const char* base;
-      if (j < BM / 8) {
-        row = m0 + 8 * j + rl;
-        row = row < M ? row : M - 1;
-        base = reinterpret_cast<const char*>(p.X);
-      } else {
-        row = n0 + 8 * (j - BM / 8) + rl;
-        row = row < N ? row : N - 1;
-        base = reinterpret_cast<const char*>(p.W);
-      }
-      src[i] = base + row * ld + chunk * 16;
-    }
-  }
-  // per-lane L2-prefetch sources: one tile row each (this wave's RPW rows)
-  const char* pfs[LPF > 0 ? LPF : 1];
-#pragma unroll
-  for (int q = 0; q < LPF; ++q) {
-    int r = q * 64 + lane;
-    r = wave * RPW + (r < RPW ? r : RPW - 1);
-    int64_t row;
-    const char* base;
-    if (r < BM) {
-      row = m0 + r;
+  for (int i = 0; i < LPW; ++i) {
+    const int j = wave * LPW + i;
+    if (j < XBLK) {                              // activation block: 8 rows x 128 B
+      const int rl = lane >> 3;
+      const int chunk = (lane & 7) ^ rl;         // logical chunk landing at slot lane & 7
+      int64_t row = m0 + 8 * j + rl;
       row = row < M ? row : M - 1;
-      base = reinterpret_cast<const char*>(p.X);
-    } else {
-      row = n0 + (r - BM);
+      src[i] = reinterpret_cast<const char*>(p.X) + row * ldx + chunk * 16;
+      sstep[i] = kRowX;
+    } else if (!kW16) {                          // weight block: 8 rows x 128 B
+      const int rl = lane >> 3;
+      const int chunk = (lane & 7) ^ rl;
+      int64_t row = n0 + 8 * (j - XBLK) + rl;
       row = row < N ? row : N - 1;
-      base = reinterpret_cast<const char*>(p.W);
+      src[i] = reinterpret_cast<const char*>(p.W) + row * ldw + chunk * 16;
+      sstep[i] = 128;
+    } else {                                     // weight block: 16 rows x 64 B
+      const int rl = lane >> 2;
+      const int chunk = (lane & 3) ^ ((rl >> 2) & 3);
+      int64_t row = n0 + 16 * (j - XBLK) + rl;
+      row = row < N ? row : N - 1;
+      src[i] = reinterpret_cast<const char*>(p.W) + row * ldw + chunk * 16;
+      sstep[i] = 64;
     }
-    pfs[q] = base + row * ld;
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
-  const uint32_t pf_dst = __builtin_amdgcn_readfirstlane(lds_base + STAGES * STAGE_BYTES + wave * LPF * 256);
-  auto prefetch = [&](int64_t kt) {
-    if constexpr (LPF > 0) {
-      const int64_t k = kt < nk ? kt : nk - 1;   // clamped so that the load count never varies
-#pragma unroll
-      for (int q = 0; q < LPF; ++q) dma4(pfs[q] + k * kRow, pf_dst + q * 256);
-    }
-  };
-  // Slice kt's loads, preceded by the L2 prefetch of slice kt + PF + STAGES - 1.
   auto issue = [&](int64_t kt) {
-    prefetch(kt + PF + STAGES - 1);
     const uint32_t dst = lds_base + (uint32_t)(kt % STAGES) * STAGE_BYTES + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i)
-      dma16(src[i] + kt * kRow, __builtin_amdgcn_readfirstlane(dst + i * 1024));
+      dma16(src[i] + kt * sstep[i], __builtin_amdgcn_readfirstlane(dst + i * 1024));
   };
 
   using Acc = typename std::conditional<kInt, v4i, v4f>::type;
@@ -206,33 +217,54 @@ gemm_dma_kernel(GemmArgs p) {
 
   const int frow = lane & 15;
   const int fk = lane >> 4;
-  // Fragments of one 64-byte K step, double-buffered in registers.
-  uint4 fa[2][FN], fb[2][FM];
+  // Fragments of one K step (64 activation bytes), double-buffered in registers.
+  using WFrag = typename std::conditional<kW16, uint2, uint4>::type;
+  WFrag fa[2][FN];
+  uint4 fb[2][FM];
   auto load_frags = [&](int buf, int64_t kt, int kk) {
     const char* xs = smem + (int)(kt % STAGES) * STAGE_BYTES;
-    const char* ws = xs + BM * kRow;
+    const char* ws = xs + XBYTES;
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
-      fa[buf][i] = *reinterpret_cast<const uint4*>(ws + swz(wn * WN + i * 16 + frow, kk * 4 + fk));
+    for (int i = 0; i < FN; ++i) {
+      const int row = wn * WN + i * 16 + frow;
+      if constexpr (kW16) {   // K step kk: weight bytes [32 kk + 8 fk, + 8)
+        const int c = 2 * kk + (fk >> 1);
+        fa[buf][i] = *reinterpret_cast<const uint2*>(ws + swz64(row, c) + 8 * (fk & 1));
+      } else {
+        fa[buf][i] = *reinterpret_cast<const uint4*>(ws + swz(row, kk * 4 + fk));
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FM; ++j)
       fb[buf][j] = *reinterpret_cast<const uint4*>(xs + swz(wm * WM + j * 16 + frow, kk * 4 + fk));
   };
   auto mma = [&](int buf) {
+    if constexpr (kW16) {
+      v8h wa[FN];
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+      for (int i = 0; i < FN; ++i) wa[i] = widen_i8x8(fa[buf][i]);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        if constexpr (kInt) {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-              *reinterpret_cast<const v4i*>(&fa[buf][i]), *reinterpret_cast<const v4i*>(&fb[buf][j]),
-              acc[i][j], 0, 0, 0);
-        } else {
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              *reinterpret_cast<const v8h*>(&fa[buf][i]), *reinterpret_cast<const v8h*>(&fb[buf][j]),
-              acc[i][j], 0, 0, 0);
+              wa[i], *reinterpret_cast<const v8h*>(&fb[buf][j]), acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          if constexpr (kInt) {
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                *reinterpret_cast<const v4i*>(&fa[buf][i]), *reinterpret_cast<const v4i*>(&fb[buf][j]),
+                acc[i][j], 0, 0, 0);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                *reinterpret_cast<const v8h*>(&fa[buf][i]), *reinterpret_cast<const v8h*>(&fb[buf][j]),
+                acc[i][j], 0, 0, 0);
+          }
         }
-      }
+    }
   };
   auto barrier = [&]() {
     compiler_fence();
@@ -246,11 +278,9 @@ gemm_dma_kernel(GemmArgs p) {
   // are read right after the barrier that publishes it, and that barrier is
   // also where the buffer of the slice just finished gets refilled (every
   // wave has drained its reads of it: lgkmcnt(0) precedes the barrier).
-  // Every slice's loads go out as one group (prefetch + slice), so the number
-  // of loads issued after a given slice is fixed: kAhead once the pipeline is
-  // full; near the end (fewer groups in flight) the waits fall back to 0.
-  if constexpr (LPF > 0)
-    for (int64_t s = 0; s < PF + STAGES - 1; ++s) prefetch(s);
+  // Every slice's loads go out as one group, so the number of loads issued
+  // after a given slice is fixed: kAhead once the pipeline is full; near the
+  // end (fewer groups in flight) the waits fall back to 0.
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue(s);
@@ -278,6 +308,46 @@ gemm_dma_kernel(GemmArgs p) {
   mma(0);
   mma(1);
 
+  // Weight-only: s_W scales the accumulators, then the LoRA product T U'^T
+  // (T = fp16(X down^T) [M, t_ld], U' = fp16(scale * up) [N, rank]) runs as
+  // extra fp16 MFMA K steps on the same accumulators.
+  if constexpr (kW16) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __fmul_rn(acc[i][j][r], swv[i][r]);
+    if (p.rank > 0) {
+      for (int r0 = 0; r0 < p.t_ld; r0 += 32) {
+        v8h ua[FN], tb[FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int64_t n = n0 + wn * WN + i * 16 + frow;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int rr = r0 + 8 * fk + e;
+            float u = 0.0f;
+            if (n < N && rr < p.rank) u = __fmul_rn(p.U[n * p.rank + rr], p.lora_scale);
+            ua[i][e] = (_Float16)u;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int64_t m = m0 + wm * WM + j * 16 + frow;
+          uint4 tv = make_uint4(0, 0, 0, 0);
+          if (m < M) tv = *reinterpret_cast<const uint4*>(p.T + m * p.t_ld + r0 + 8 * fk);
+          tb[j] = *reinterpret_cast<const v8h*>(&tv);
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ua[i], tb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
   // ---------------------------------------------------------------- epilogue
   // The finished tile goes through LDS (the ring is free now) so that global
   // stores are whole 16-byte chunks of contiguous output rows.
@@ -304,6 +374,13 @@ gemm_dma_kernel(GemmArgs p) {
             // Y = fp16( fp32(A) * fp32(s_X * s_W) [+ bias] ), no contraction
             const float sc = __fmul_rn(sxv[j], swv[i][r]);
             float y = __fmul_rn((float)acc[i][j][r], sc);
+            if (p.bias) y = __fadd_rn(y, bsv[i][r]);
+            h[r] = __float2half_rn(y);
+          }
+        } else if constexpr (kW16) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float y = acc[i][j][r];
             if (p.bias) y = __fadd_rn(y, bsv[i][r]);
             h[r] = __float2half_rn(y);
           }
@@ -341,14 +418,13 @@ gemm_dma_kernel(GemmArgs p) {
   }
 }
 
-template <GemmMode MODE, int WAM, int WAN, int FM, int FN, int ST, int PF>
+template <GemmMode MODE, int WAM, int WAN, int FM, int FN, int ST>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int BM = 16 * FM * WAM, BN = 16 * FN * WAN;
-  constexpr int NW = WAM * WAN;
-  constexpr int LPF = PF >= 0 ? ((BM + BN) / NW + 63) / 64 : 0;
+  constexpr int kRowW = MODE == GemmMode::kW8A16 ? 64 : 128;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const size_t lds = (size_t)ST * (BM + BN) * kRow + (size_t)NW * LPF * 256;
-  auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST, PF>;
+  const size_t lds = (size_t)ST * ((size_t)BM * kRowX + (size_t)BN * kRowW);
+  auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -365,21 +441,15 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 template <GemmMode MODE>
 hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
   switch (cfg) {
-    case 0: return launch_cfg<MODE, 2, 2, 4, 4, 3, -1>(a, stream);   // 128x128
-    case 1: return launch_cfg<MODE, 2, 2, 4, 4, 4, -1>(a, stream);   // 128x128, 4 stages
-    case 2: return launch_cfg<MODE, 2, 2, 8, 4, 3, -1>(a, stream);   // 256x128
-    case 3: return launch_cfg<MODE, 2, 2, 4, 8, 3, -1>(a, stream);   // 128x256
-    case 4: return launch_cfg<MODE, 2, 1, 4, 4, 4, -1>(a, stream);   // 128x64 (2 waves)
-    case 5: return launch_cfg<MODE, 1, 2, 4, 4, 4, -1>(a, stream);   // 64x128 (2 waves)
-    case 6: return launch_cfg<MODE, 1, 1, 4, 4, 4, -1>(a, stream);   // 64x64 (1 wave)
-    case 7: return launch_cfg<MODE, 2, 2, 2, 4, 4, -1>(a, stream);   // 64x128
-    case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4, -1>(a, stream);   // 128x64
-    case 9: return launch_cfg<MODE, 2, 2, 4, 4, 3, 2>(a, stream);    // 128x128 with L2 prefetch
-    case 10: return launch_cfg<MODE, 2, 2, 8, 4, 3, 2>(a, stream);   // 256x128 with L2 prefetch
-    case 11: return launch_cfg<MODE, 2, 2, 4, 2, 4, 3>(a, stream);   // 128x64 with L2 prefetch
-    case 12: return launch_cfg<MODE, 2, 2, 4, 2, 5, -1>(a, stream);  // 128x64, 5 stages
-    case 13: return launch_cfg<MODE, 2, 2, 4, 2, 6, -1>(a, stream);  // 128x64, 6 stages
-    case 14: return launch_cfg<MODE, 2, 2, 4, 4, 5, -1>(a, stream);  // 128x128, 5 stages
+    case 0: return launch_cfg<MODE, 2, 2, 4, 4, 3>(a, stream);   // 128x128
+    case 1: return launch_cfg<MODE, 2, 2, 4, 4, 4>(a, stream);   // 128x128, 4 stages
+    case 2: return launch_cfg<MODE, 2, 2, 8, 4, 3>(a, stream);   // 256x128
+    case 3: return launch_cfg<MODE, 2, 2, 4, 8, 3>(a, stream);   // 128x256
+    case 4: return launch_cfg<MODE, 2, 1, 4, 4, 4>(a, stream);   // 128x64 (2 waves)
+    case 5: return launch_cfg<MODE, 1, 2, 4, 4, 4>(a, stream);   // 64x128 (2 waves)
+    case 6: return launch_cfg<MODE, 1, 1, 4, 4, 4>(a, stream);   // 64x64 (1 wave)
+    case 7: return launch_cfg<MODE, 2, 2, 2, 4, 4>(a, stream);   // 64x128
+    case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4>(a, stream);   // 128x64
     default: return hipErrorInvalidValue;
   }
 }
@@ -387,5 +457,6 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
 template hipError_t launch_gemm_dma_cfg<GemmMode::kI8toI32>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm_dma_cfg<GemmMode::kI8toF16>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm_dma_cfg<GemmMode::kF16>(const GemmArgs&, int, hipStream_t);
+template hipError_t launch_gemm_dma_cfg<GemmMode::kW8A16>(const GemmArgs&, int, hipStream_t);
 
 }  // namespace convrot

@@ -25,7 +25,7 @@ struct GemmArgs {
 template <GemmMode MODE>
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
-// Pipelined direct-to-LDS GEMM (int8 and fp16 modes) with an explicit tile
+// Pipelined direct-to-LDS GEMM (every mode) with an explicit tile
 // configuration id, and the id the library picks for a problem size.
 template <GemmMode MODE>
 hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream);
