@@ -238,17 +238,24 @@ gemm_dma_kernel(GemmArgs p) {
     for (int j = 0; j < FM; ++j)
       fb[buf][j] = *reinterpret_cast<const uint4*>(xs + swz(wm * WM + j * 16 + frow, kk * 4 + fk));
   };
+  // Weight-only: the widened weight fragments of a K step are produced right
+  // after the MFMAs of the previous step are issued, so the VALU work runs
+  // while the matrix cores are busy instead of in front of them.
+  v8h wa[2][kW16 ? FN : 1];
+  auto widen = [&](int buf) {
+    if constexpr (kW16) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) wa[buf][i] = widen_i8x8(fa[buf][i]);
+    }
+  };
   auto mma = [&](int buf) {
     if constexpr (kW16) {
-      v8h wa[FN];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) wa[i] = widen_i8x8(fa[buf][i]);
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              wa[i], *reinterpret_cast<const v8h*>(&fb[buf][j]), acc[i][j], 0, 0, 0);
+              wa[buf][i], *reinterpret_cast<const v8h*>(&fb[buf][j]), acc[i][j], 0, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < FN; ++i)
@@ -289,6 +296,7 @@ gemm_dma_kernel(GemmArgs p) {
   barrier();
   if (STAGES - 1 < nk) issue(STAGES - 1);
   load_frags(0, 0, 0);
+  widen(0);
 
   // The last slice is peeled off so that the loop body has a single path into
   // its second MFMA group: the LDS-read counter then only waits for reads that
@@ -296,6 +304,7 @@ gemm_dma_kernel(GemmArgs p) {
   for (int64_t kt = 0; kt + 1 < nk; ++kt) {
     load_frags(1, kt, 1);
     mma(0);
+    widen(1);
     if (kt + STAGES - 1 < nk) wait_vmcnt<kAhead>();
     else wait_vmcnt<0>();
     wait_lgkm0();
@@ -303,9 +312,11 @@ gemm_dma_kernel(GemmArgs p) {
     if (kt + STAGES < nk) issue(kt + STAGES);
     load_frags(0, kt + 1, 0);
     mma(1);
+    widen(0);
   }
   load_frags(1, nk - 1, 1);
   mma(0);
+  widen(1);
   mma(1);
 
   // Weight-only: s_W scales the accumulators, then the LoRA product T U'^T
@@ -324,13 +335,19 @@ gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
           const int64_t n = n0 + wn * WN + i * 16 + frow;
+          const int rb = r0 + 8 * fk;
+          float u[8];
+          if (n < N && rb + 8 <= p.rank && (p.rank & 3) == 0) {
+            const float4* up = reinterpret_cast<const float4*>(p.U + n * p.rank + rb);
+            const float4 u0 = up[0], u1 = up[1];
+            u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w;
+            u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
+          } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int rr = r0 + 8 * fk + e;
-            float u = 0.0f;
-            if (n < N && rr < p.rank) u = __fmul_rn(p.U[n * p.rank + rr], p.lora_scale);
-            ua[i][e] = (_Float16)u;
+            for (int e = 0; e < 8; ++e) u[e] = (n < N && rb + e < p.rank) ? p.U[n * p.rank + rb + e] : 0.0f;
           }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ua[i][e] = (_Float16)__fmul_rn(u[e], p.lora_scale);
         }
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
