@@ -48,12 +48,18 @@
 namespace convrot {
 namespace {
 
-constexpr int kRowX = 128;  // activation bytes of one K slice per row
-
-// 128-byte rows: chunk c of row r at slot c ^ (r & 7)
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
-// 64-byte rows (weight-only int8 weights): chunk c of row r at slot c ^ ((r >> 2) & 3)
-__device__ __forceinline__ int swz64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// LDS row layouts, by row bytes RB (the K slice of one tile row): 16-byte
+// chunk c of row r sits at slot c ^ key(r), key = r & 15 (256-byte rows),
+// r & 7 (128-byte rows) or (r >> 2) & 3 (64-byte rows: 16 rows per 1 KiB
+// block).  In each case the 16 rows a fragment read touches at one chunk
+// index land in distinct banks, and so do the lanes of one direct load.
+template <int RB>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (RB == 64) return (row >> 2) & 3;
+  else return row & (RB / 16 - 1);
+}
+template <int RB>
+__device__ __forceinline__ int swz(int row, int chunk) { return row * RB + ((chunk ^ swz_key<RB>(row)) << 4); }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -101,7 +107,7 @@ __device__ __forceinline__ v8h widen_i8x8(uint2 w) {
   return r;
 }
 
-template <GemmMode MODE, int WAVES_M, int WAVES_N, int FM, int FN, int STAGES>
+template <GemmMode MODE, int WAVES_M, int WAVES_N, int FM, int FN, int STAGES, int XS>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_dma_kernel(GemmArgs p) {
   constexpr bool kInt = (MODE == GemmMode::kI8toI32 || MODE == GemmMode::kI8toF16);
@@ -109,9 +115,12 @@ gemm_dma_kernel(GemmArgs p) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = 16 * FM, WN = 16 * FN;     // wave tile (m, n)
   constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
-  constexpr int kRowW = kW16 ? 64 : 128;        // weight bytes of one K slice per row
+  constexpr int kRowX = XS;                     // activation bytes of one K slice per row
+  constexpr int kRowW = kW16 ? XS / 2 : XS;     // weight bytes of one K slice per row
+  constexpr int NKK = XS / 64;                  // K steps (64 activation bytes) per slice
+  constexpr int XROWS = 1024 / kRowX;           // activation rows per 1 KiB block
   constexpr int WROWS = 1024 / kRowW;           // weight rows per 1 KiB block
-  constexpr int XBLK = BM / 8;                  // activation blocks per slice
+  constexpr int XBLK = BM / XROWS;              // activation blocks per slice
   constexpr int NBLK = XBLK + BN / WROWS;       // 1 KiB direct loads per slice
   constexpr int LPW = NBLK / NW;                // per wave per slice
   constexpr int XBYTES = BM * kRowX;
@@ -120,7 +129,8 @@ gemm_dma_kernel(GemmArgs p) {
   constexpr int kElemW = (MODE == GemmMode::kF16) ? 2 : 1;
   constexpr int kAhead = (STAGES - 2) * LPW;    // loads issued after the awaited slice
   static_assert(NBLK % NW == 0, "blocks must split evenly over waves");
-  static_assert(BN % WROWS == 0, "whole weight blocks");
+  static_assert(BN % WROWS == 0 && BM % XROWS == 0, "whole blocks");
+  static_assert(NKK % 2 == 0, "fragment buffers alternate per K step");
   static_assert(STAGES >= 3 && kAhead < 64, "pipeline depth");
 
   extern __shared__ __align__(16) char smem[];
@@ -177,27 +187,24 @@ gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int j = wave * LPW + i;
-    if (j < XBLK) {                              // activation block: 8 rows x 128 B
-      const int rl = lane >> 3;
-      const int chunk = (lane & 7) ^ rl;         // logical chunk landing at slot lane & 7
-      int64_t row = m0 + 8 * j + rl;
+    if (j < XBLK) {                              // activation block: XROWS rows
+      const int rl = lane / (kRowX / 16);        // row within the block
+      const int slot = lane % (kRowX / 16);
+      const int trow = XROWS * j + rl;           // row within the tile
+      const int chunk = slot ^ swz_key<kRowX>(trow);   // logical chunk landing at `slot`
+      int64_t row = m0 + trow;
       row = row < M ? row : M - 1;
       src[i] = reinterpret_cast<const char*>(p.X) + row * ldx + chunk * 16;
       sstep[i] = kRowX;
-    } else if (!kW16) {                          // weight block: 8 rows x 128 B
-      const int rl = lane >> 3;
-      const int chunk = (lane & 7) ^ rl;
-      int64_t row = n0 + 8 * (j - XBLK) + rl;
+    } else {                                     // weight block: WROWS rows
+      const int rl = lane / (kRowW / 16);
+      const int slot = lane % (kRowW / 16);
+      const int trow = WROWS * (j - XBLK) + rl;
+      const int chunk = slot ^ swz_key<kRowW>(trow);
+      int64_t row = n0 + trow;
       row = row < N ? row : N - 1;
       src[i] = reinterpret_cast<const char*>(p.W) + row * ldw + chunk * 16;
-      sstep[i] = 128;
-    } else {                                     // weight block: 16 rows x 64 B
-      const int rl = lane >> 2;
-      const int chunk = (lane & 3) ^ ((rl >> 2) & 3);
-      int64_t row = n0 + 16 * (j - XBLK) + rl;
-      row = row < N ? row : N - 1;
-      src[i] = reinterpret_cast<const char*>(p.W) + row * ldw + chunk * 16;
-      sstep[i] = 64;
+      sstep[i] = kRowW;
     }
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
@@ -229,14 +236,14 @@ gemm_dma_kernel(GemmArgs p) {
       const int row = wn * WN + i * 16 + frow;
       if constexpr (kW16) {   // K step kk: weight bytes [32 kk + 8 fk, + 8)
         const int c = 2 * kk + (fk >> 1);
-        fa[buf][i] = *reinterpret_cast<const uint2*>(ws + swz64(row, c) + 8 * (fk & 1));
+        fa[buf][i] = *reinterpret_cast<const uint2*>(ws + swz<kRowW>(row, c) + 8 * (fk & 1));
       } else {
-        fa[buf][i] = *reinterpret_cast<const uint4*>(ws + swz(row, kk * 4 + fk));
+        fa[buf][i] = *reinterpret_cast<const uint4*>(ws + swz<kRowW>(row, kk * 4 + fk));
       }
     }
 #pragma unroll
     for (int j = 0; j < FM; ++j)
-      fb[buf][j] = *reinterpret_cast<const uint4*>(xs + swz(wm * WM + j * 16 + frow, kk * 4 + fk));
+      fb[buf][j] = *reinterpret_cast<const uint4*>(xs + swz<kRowX>(wm * WM + j * 16 + frow, kk * 4 + fk));
   };
   // Weight-only: the widened weight fragments of a K step are produced right
   // after the MFMAs of the previous step are issued, so the VALU work runs
@@ -301,10 +308,14 @@ gemm_dma_kernel(GemmArgs p) {
   // The last slice is peeled off so that the loop body has a single path into
   // its second MFMA group: the LDS-read counter then only waits for reads that
   // group actually consumes, not for the next slice's reads issued before it.
+  // K steps alternate between the two fragment buffers (NKK is even).
   for (int64_t kt = 0; kt + 1 < nk; ++kt) {
-    load_frags(1, kt, 1);
-    mma(0);
-    widen(1);
+#pragma unroll
+    for (int kk = 0; kk + 1 < NKK; ++kk) {
+      load_frags((kk + 1) & 1, kt, kk + 1);
+      mma(kk & 1);
+      widen((kk + 1) & 1);
+    }
     if (kt + STAGES - 1 < nk) wait_vmcnt<kAhead>();
     else wait_vmcnt<0>();
     wait_lgkm0();
@@ -314,9 +325,12 @@ gemm_dma_kernel(GemmArgs p) {
     mma(1);
     widen(0);
   }
-  load_frags(1, nk - 1, 1);
-  mma(0);
-  widen(1);
+#pragma unroll
+  for (int kk = 0; kk + 1 < NKK; ++kk) {
+    load_frags((kk + 1) & 1, nk - 1, kk + 1);
+    mma(kk & 1);
+    widen((kk + 1) & 1);
+  }
   mma(1);
 
   // Weight-only: s_W scales the accumulators, then the LoRA product T U'^T
@@ -435,13 +449,13 @@ gemm_dma_kernel(GemmArgs p) {
   }
 }
 
-template <GemmMode MODE, int WAM, int WAN, int FM, int FN, int ST>
+template <GemmMode MODE, int WAM, int WAN, int FM, int FN, int ST, int XS = 128>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int BM = 16 * FM * WAM, BN = 16 * FN * WAN;
-  constexpr int kRowW = MODE == GemmMode::kW8A16 ? 64 : 128;
+  constexpr int kRowW = MODE == GemmMode::kW8A16 ? XS / 2 : XS;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const size_t lds = (size_t)ST * ((size_t)BM * kRowX + (size_t)BN * kRowW);
-  auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST>;
+  const size_t lds = (size_t)ST * ((size_t)BM * XS + (size_t)BN * kRowW);
+  auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST, XS>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
