@@ -9,9 +9,12 @@ namespace convrot {
 
 // 256x128 tiles read half the operand bytes per output of 128x64 tiles,
 // which pays once they still give most of the 256 CUs a tile; otherwise
-// 128x64 tiles spread the work wider.
+// 128x64 tiles spread the work wider.  With few rows (M <= 128) the product
+// streams the weights, and 32x64 tiles keep the activation loads from being
+// mostly padding while giving four times as many workgroups.
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
   (void)mode; (void)K;
+  if (M <= 128) return 9;
   const int64_t big = ((M + 255) / 256) * ((N + 127) / 128);
   return big >= 160 ? 2 : 8;
 }

@@ -481,6 +481,10 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 6: return launch_cfg<MODE, 1, 1, 4, 4, 4>(a, stream);   // 64x64 (1 wave)
     case 7: return launch_cfg<MODE, 2, 2, 2, 4, 4>(a, stream);   // 64x128
     case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4>(a, stream);   // 128x64
+    case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4>(a, stream);   // 32x64 (few rows)
+    case 10: return launch_cfg<MODE, 2, 2, 2, 2, 4>(a, stream);  // 64x64
+    case 11: return launch_cfg<MODE, 1, 4, 2, 2, 4>(a, stream);  // 32x128
+    case 12: return launch_cfg<MODE, 1, 4, 2, 4, 3>(a, stream);  // 32x256
     default: return hipErrorInvalidValue;
   }
 }
