@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-compare", action="store_true", help="skip the W8A16 / fp16 comparison sweeps")
+    p.add_argument("--no-m-sweep", action="store_true", help="skip the row-count sweep on the two large shapes")
     p.add_argument("--profile-kernels", action="store_true",
                    help="run one eager W8A8 step plus a calibration copy of known size and exit "
                         "(the program to run under rocprofv3 --pmc)")
@@ -165,6 +166,52 @@ def summarize_pmc(fetch_csv, write_csv):
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+
+
+M_SWEEP = (1, 16, 128, 1024, 4096, 16384)
+M_SWEEP_SHAPES = ((8192, 2048), (2048, 8192))
+
+
+def m_sweep(cr, L, stream, dev):
+    """W8A8 end to end and fp16 F.linear at several row counts on the two large
+    shapes (hot buffers; median of 5 sets of 10 calls, graph-captured)."""
+    import torch
+    import torch.nn.functional as F
+    import workload as wl
+    rows = []
+    for (N, K) in M_SWEEP_SHAPES:
+        w = wl.make_weights(N, K, seed=0).to(dev)
+        qw, sw = cr.quantize_weights(w)
+        w16 = w.to(torch.float16)
+        del w
+        for M in M_SWEEP:
+            x = wl.make_activations(M, K, seed=0).to(dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            ws = torch.empty(cr.workspace_bytes(cr.PATH_W8A8, M, N, K), dtype=torch.uint8, device=dev)
+
+            def w8a8():
+                h = torch.cuda.current_stream().cuda_stream
+                for _ in range(10):
+                    st = L.convrot_linear_w8a8(x.data_ptr(), M, K, qw.data_ptr(), sw.data_ptr(), N, None,
+                                               y.data_ptr(), ws.data_ptr(), ws.numel(), h)
+                    if st:
+                        raise RuntimeError(L.convrot_status_string(st).decode())
+
+            def f16():
+                for _ in range(10):
+                    F.linear(x, w16)
+
+            row = {"N": N, "K": K, "M": M}
+            for name, fn in (("w8a8_us", w8a8), ("fp16_torch_linear_us", f16)):
+                g = capture(fn, stream)
+                row[name] = round(median_sets(g, 5, stream) / 10 * 1e3, 3)
+                del g
+            row["w8a8_tops"] = round(2.0 * M * N * K / (row["w8a8_us"] * 1e-6) / 1e12, 1)
+            row["w8a8_weight_gbs"] = round(N * K / (row["w8a8_us"] * 1e-6) / 1e9, 1)
+            rows.append(row)
+            del x, y, ws
+        del qw, sw, w16
+    return rows
 
 
 def cpu_baseline(shapes, M):
@@ -392,6 +439,11 @@ def main():
                 compare[name] = {"ms_per_step": round(t, 4),
                                  "tops": round(ops_step / (t * 1e-3) / 1e12, 1)}
 
+        msweep = None
+        if not args.no_m_sweep:
+            log("row-count sweep on 8192x2048 and 2048x8192")
+            msweep = m_sweep(cr, L, stream, dev)
+
     n_launch = sum(s["layers"] for s in per_shape)
     traffic = load_traffic(GEMM_SRC)
     achieved = ops_step / (ms_gemm * 1e-3) / 1e12
@@ -437,6 +489,7 @@ def main():
         "per_shape": shape_rows,
         "weighted_total_ms": round(sum(r["w8a8_us"] * r["layers"] for r in shape_rows) / 1e3, 4),
         "compare": compare,
+        "m_sweep": msweep,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host")

@@ -75,7 +75,11 @@ size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_
   if (M < 0 || N < 0 || K < 0 || lora_rank < 0 || lora_rank > CONVROT_LORA_RANK_MAX) return (size_t)-1;
   if (M == 0 || N == 0) return 0;
   if (!k_ok(K)) return (size_t)-1;
-  if (path == CONVROT_PATH_W8A8) return round256((size_t)M * K) + round256((size_t)M * 4);
+  if (path == CONVROT_PATH_W8A8) {
+    const int64_t splits = w8a8_splits(M, N, K);
+    return round256((size_t)M * K) + round256((size_t)M * 4) +
+           (splits > 1 ? round256((size_t)splits * M * N * 4) : 0);
+  }
   if (path == CONVROT_PATH_W8A16)
     return round256((size_t)M * K * 2) + round256((size_t)M * lora_ld(lora_rank) * 2);
   return (size_t)-1;
@@ -202,13 +206,23 @@ convrot_status convrot_linear_w8a8(const void* X, int64_t M, int64_t K, const in
       overlap(workspace, need, bias, bias ? (size_t)N * 4 : 0))
     return CONVROT_ERR_INVALID_ARG;
   if (convrot_status st = check_device()) return st;
-  int8_t* QX = reinterpret_cast<int8_t*>(workspace);
-  float* sX = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + round256((size_t)M * K));
+  char* ws = reinterpret_cast<char*>(workspace);
+  int8_t* QX = reinterpret_cast<int8_t*>(ws);
+  float* sX = reinterpret_cast<float*>(ws + round256((size_t)M * K));
   hipStream_t s = as_stream(stream);
   if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s))) return st;
   GemmArgs g{};
   g.X = QX; g.W = Q_W; g.sX = sX; g.sW = s_W; g.bias = bias; g.out = Y;
   g.M = M; g.N = N; g.K = K;
+  const int64_t splits = w8a8_splits(M, N, K);
+  if (splits > 1) {   // few rows: int32 partials over K splits, then the scale epilogue
+    int32_t* parts = reinterpret_cast<int32_t*>(ws + round256((size_t)M * K) + round256((size_t)M * 4));
+    g.out = parts;
+    g.sX = nullptr; g.sW = nullptr; g.bias = nullptr;
+    g.kc = K / splits;
+    if (convrot_status st = launched(launch_gemm<GemmMode::kI8toI32>(g, s))) return st;
+    return launched(launch_splitk_epilogue(parts, splits, sX, s_W, bias, M, N, Y, s));
+  }
   return launched(launch_gemm<GemmMode::kI8toF16>(g, s));
 }
 

@@ -139,7 +139,11 @@ gemm_dma_kernel(GemmArgs p) {
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t M = p.M, N = p.N;
+  // Split K (grid y > 1, int32 output only): split z takes K values
+  // [z kc, (z + 1) kc) of rows of stride p.K and writes its own partial A.
+  const int64_t K = p.kc ? p.kc : p.K;
+  const int64_t kz = (int64_t)blockIdx.y * K;
   const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t T = tiles_m * tiles_n;
@@ -153,9 +157,9 @@ gemm_dma_kernel(GemmArgs p) {
   const int64_t tile_n = t / tiles_m;
   const int64_t tile_m = t - tile_n * tiles_m;
   const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
-  const int64_t ldx = K * kElemX;                // row bytes of the activations
-  const int64_t ldw = K * kElemW;                // row bytes of the weights
-  const int64_t nk = ldx / kRowX;
+  const int64_t ldx = p.K * kElemX;              // row bytes of the activations
+  const int64_t ldw = p.K * kElemW;              // row bytes of the weights
+  const int64_t nk = K * kElemX / kRowX;
 
   // Epilogue operands are fetched first so that their latency hides behind the
   // main loop (issued before the first direct load, they also complete first).
@@ -194,7 +198,7 @@ gemm_dma_kernel(GemmArgs p) {
       const int chunk = slot ^ swz_key<kRowX>(trow);   // logical chunk landing at `slot`
       int64_t row = m0 + trow;
       row = row < M ? row : M - 1;
-      src[i] = reinterpret_cast<const char*>(p.X) + row * ldx + chunk * 16;
+      src[i] = reinterpret_cast<const char*>(p.X) + row * ldx + kz * kElemX + chunk * 16;
       sstep[i] = kRowX;
     } else {                                     // weight block: WROWS rows
       const int rl = lane / (kRowW / 16);
@@ -203,7 +207,7 @@ gemm_dma_kernel(GemmArgs p) {
       const int chunk = slot ^ swz_key<kRowW>(trow);
       int64_t row = n0 + trow;
       row = row < N ? row : N - 1;
-      src[i] = reinterpret_cast<const char*>(p.W) + row * ldw + chunk * 16;
+      src[i] = reinterpret_cast<const char*>(p.W) + row * ldw + kz * kElemW + chunk * 16;
       sstep[i] = kRowW;
     }
   }
@@ -430,7 +434,7 @@ gemm_dma_kernel(GemmArgs p) {
   constexpr int CPR = BN * kOut / 16;             // 16-byte chunks per tile row
   constexpr int NTH = 64 * NW;
   const bool vec_rows = ((N * kOut) % 16) == 0;   // every output row starts 16-byte aligned
-  char* outb = reinterpret_cast<char*>(p.out);
+  char* outb = reinterpret_cast<char*>(p.out) + (int64_t)blockIdx.y * M * N * kOut;
 #pragma unroll 4
   for (int c = tid; c < BM * CPR; c += NTH) {
     const int rl = c / CPR, cc = c - rl * CPR;
@@ -461,7 +465,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(fn, dim3((unsigned)tiles), dim3(64 * WAM * WAN), lds, stream, a);
+  const unsigned splits = a.kc ? (unsigned)(a.K / a.kc) : 1u;
+  hipLaunchKernelGGL(fn, dim3((unsigned)tiles, splits), dim3(64 * WAM * WAN), lds, stream, a);
   return hipGetLastError();
 }
 

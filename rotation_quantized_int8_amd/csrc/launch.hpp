@@ -18,8 +18,9 @@ struct GemmArgs {
   float lora_scale;
   int rank;             // LoRA rank (0 = none)
   int t_ld;             // row stride of T (rank rounded up to 32)
-  void* out;            // [M, N] int32 or fp16
+  void* out;            // [M, N] int32 or fp16; with kc: [K / kc, M, N] int32 partials
   int64_t M, N, K;
+  int64_t kc;           // 0, or K per split (kI8toI32 only; a multiple of 256 dividing K)
 };
 
 template <GemmMode MODE>
@@ -30,6 +31,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 template <GemmMode MODE>
 hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream);
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K);
+
+// Split-K plan of the W8A8 linear: number of K splits (1 = none) for a size.
+int64_t w8a8_splits(int64_t M, int64_t N, int64_t K);
+// Y = fp16(fp32(sum_z A_z) * fp32(s_X s_W) [+ bias]) from the int32 partials.
+hipError_t launch_splitk_epilogue(const int32_t* parts, int64_t splits, const float* sX,
+                                  const float* sW, const float* bias, int64_t M, int64_t N,
+                                  void* Y, hipStream_t stream);
 
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* QW, float* sW,
                                    hipStream_t stream);

@@ -41,6 +41,8 @@ def test_workspace_bytes(L):
     assert L.convrot_workspace_bytes(1, 4, 8, 256, 0) == 2048
     assert L.convrot_workspace_bytes(1, 4, 8, 256, 32) == 2048 + 256
     assert L.convrot_workspace_bytes(0, 0, 5, 256, 0) == 0
+    # few rows and a small tile grid: room for 8 K-split int32 partials
+    assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 0) == 16 * 8192 + 256 + 8 * 16 * 2048 * 4
     bad = ctypes.c_size_t(-1).value
     assert L.convrot_workspace_bytes(0, 4, 4, 255, 0) == bad
     assert L.convrot_workspace_bytes(0, 4, 4, 131072 + 256, 0) == bad

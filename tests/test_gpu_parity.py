@@ -252,6 +252,16 @@ def test_linear_w8a8_m_sweep(M, N, K, dist):
     assert mism == 0 and emax == 0.0
 
 
+@pytest.mark.parametrize("M,N,K,bias", [(32, 2048, 2048, False), (5, 200, 4096, True),
+                                        (16, 2048, 8192, True), (64, 1000, 2048, False)])
+def test_linear_w8a8_split_k_bitexact(M, N, K, bias):
+    # few rows: K is split over workgroups and the int32 partials are summed
+    # in a separate epilogue; the result must equal the unsplit definition
+    _say(f"linear w8a8 split-K M={M} N={N} K={K} bias={bias}")
+    mism, emax, rel = _w8a8_case(M, N, K, seed=M * 7 + N, bias=bias)
+    assert mism == 0 and emax == 0.0
+
+
 def test_linear_w8a8_empty_1d_and_leading_dims():
     _say("linear w8a8 empty / 1-D / 3-D")
     K, N = 512, 40
