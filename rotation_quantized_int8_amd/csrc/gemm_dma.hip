@@ -35,8 +35,9 @@
 //
 // Tile order is XCD-aware: workgroups are dispatched round-robin over the 8
 // XCDs, so the i-th workgroup on XCD x gets the i-th tile of a contiguous
-// range, ordered with M fastest.  Each XCD then streams a few weight panels
-// through its own L2 once while the activation tiles are shared.
+// range of a grouped order (row tiles in groups covering 1024 rows, N-major
+// inside a group).  Each XCD then streams a few weight panels through its own
+// L2 while its resident workgroups share the activation bands.
 //
 // Rows past M or N are clamped to the last valid row for the loads (so every
 // load is in bounds) and dropped in the epilogue.
@@ -154,8 +155,16 @@ gemm_dma_kernel(GemmArgs p) {
     const int64_t per = T >> 3, rem = T & 7;
     t = x * per + (x < rem ? x : rem) + i;
   }
-  const int64_t tile_n = t / tiles_m;
-  const int64_t tile_m = t - tile_n * tiles_m;
+  // Grouped order: tiles run in groups of GM row tiles (1024 rows), N-major
+  // inside a group, so the workgroups resident on one XCD at a time share a
+  // few activation bands and weight panels in that XCD's L2 even when M is
+  // large.  With M <= 1024 this is the plain M-fastest order.
+  constexpr int64_t GM = BM >= 1024 ? 1 : 1024 / BM;
+  const int64_t in_group = GM * tiles_n;
+  const int64_t first_m = (t / in_group) * GM;
+  const int64_t gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int64_t tile_m = first_m + (t % in_group) % gsize;
+  const int64_t tile_n = (t % in_group) / gsize;
   const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
   const int64_t ldx = p.K * kElemX;              // row bytes of the activations
   const int64_t ldw = p.K * kElemW;              // row bytes of the weights
