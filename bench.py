@@ -290,16 +290,23 @@ def main():
         ws8 = torch.empty(cr.workspace_bytes(cr.PATH_W8A8, M, N, K), dtype=torch.uint8, device=dev)
         ws16 = torch.empty(cr.workspace_bytes(cr.PATH_W8A16, M, N, K, wl.LORA_RANK), dtype=torch.uint8, device=dev)
         down, up = wl.make_lora(N, K, seed=0)
+        # Q_X / s_X of the stand-alone prologue and GEMM legs
+        qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
         per_shape.append(dict(N=N, K=K, layers=layers, x=x, qws=qws, sw=sw, w16=w16, y=y, ws8=ws8,
-                              ws16=ws16, down=down.to(dev), up=up.to(dev),
-                              qx=ws8[:M * K].view(torch.int8).view(M, K),
-                              sx=ws8[(M * K + 255) // 256 * 256:][:4 * M].view(torch.float32)))
+                              ws16=ws16, down=down.to(dev), up=up.to(dev), qx=qx, sx=sx))
     torch.cuda.synchronize()
     ops_step = sum(2.0 * M * s["N"] * s["K"] * s["layers"] for s in per_shape)
 
     f8a8 = L.convrot_linear_w8a8
     fpro = L.convrot_act_quant
     fgemm = L.convrot_gemm_i8_f16
+    for s in per_shape:   # Q_X / s_X for the GEMM-only legs
+        st = fpro(s["x"].data_ptr(), M, s["K"], s["qx"].data_ptr(), s["sx"].data_ptr(),
+                  torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise RuntimeError(L.convrot_status_string(st).decode())
+    torch.cuda.synchronize()
 
     def w8a8_step():
         h = torch.cuda.current_stream().cuda_stream

@@ -38,12 +38,20 @@ __device__ __forceinline__ __half f64_to_f16_rn(double d) {
   return __float2half_rn(f);
 }
 
+// One DPP lane permutation of a float inside each 16-lane row of the wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float warp_max16(float v) {
-  // max over the 16 lanes of an aligned 16-lane segment
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
+  // max over the 16 lanes of an aligned 16-lane segment (a DPP row), by
+  // register-to-register lane permutations: swap neighbours (quad_perm
+  // [1,0,3,2]), swap pairs ([2,3,0,1]), mirror each 8-lane half, mirror the row
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
   return v;
 }
 

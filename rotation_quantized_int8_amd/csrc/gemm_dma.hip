@@ -13,7 +13,10 @@
 // bytes per row (128 int8 or 64 fp16 values) through a ring of STAGES LDS
 // buffers filled by direct global->LDS loads (global_load_lds_dwordx4:
 // 64 lanes x 16 B = one 1 KiB block per instruction, no register staging).
-// STAGES-1 slices are in flight while one is consumed.  128-byte LDS rows
+// STAGES-1 slices are in flight while one is consumed.  The ring holds the
+// activation rows of every stage first, then the weight rows of every stage,
+// and each wave loads the same number of activation blocks and of weight
+// blocks per slice.  128-byte LDS rows
 // have their 16-byte chunks XOR-swizzled by (row & 7); the weight-only
 // mode's int8 weight rows are 64 bytes per slice (16 rows per block) with
 // their chunks swizzled by ((row >> 2) & 3).  Both make the fills and the
@@ -122,14 +125,16 @@ gemm_dma_kernel(GemmArgs p) {
   constexpr int XROWS = 1024 / kRowX;           // activation rows per 1 KiB block
   constexpr int WROWS = 1024 / kRowW;           // weight rows per 1 KiB block
   constexpr int XBLK = BM / XROWS;              // activation blocks per slice
-  constexpr int NBLK = XBLK + BN / WROWS;       // 1 KiB direct loads per slice
-  constexpr int LPW = NBLK / NW;                // per wave per slice
-  constexpr int XBYTES = BM * kRowX;
-  constexpr int STAGE_BYTES = XBYTES + BN * kRowW;
+  constexpr int WBLK = BN / WROWS;              // weight blocks per slice
+  constexpr int XL = XBLK / NW, WL = WBLK / NW; // per wave per slice
+  constexpr int LPW = XL + WL;
+  constexpr int XBYTES = BM * kRowX;            // one stage of activation rows
+  constexpr int WBYTES = BN * kRowW;            // one stage of weight rows
+  constexpr int WBASE = STAGES * XBYTES;        // LDS offset of the weight stages
   constexpr int kElemX = kInt ? 1 : 2;
   constexpr int kElemW = (MODE == GemmMode::kF16) ? 2 : 1;
   constexpr int kAhead = (STAGES - 2) * LPW;    // loads issued after the awaited slice
-  static_assert(NBLK % NW == 0, "blocks must split evenly over waves");
+  static_assert(XBLK % NW == 0 && WBLK % NW == 0, "blocks must split evenly over waves");
   static_assert(BN % WROWS == 0 && BM % XROWS == 0, "whole blocks");
   static_assert(NKK % 2 == 0, "fragment buffers alternate per K step");
   static_assert(STAGES >= 3 && kAhead < 64, "pipeline depth");
@@ -194,38 +199,49 @@ gemm_dma_kernel(GemmArgs p) {
       }
   }
 
-  // per-lane direct-load sources for this wave's blocks
-  const char* src[LPW];
-  int sstep[LPW];                                // bytes per slice of that source
+  // Per-lane direct-load sources of this wave's blocks: activation blocks
+  // j = wave XL + i (XROWS rows each) and weight blocks j = wave WL + i
+  // (WROWS rows each) of every slice.
+  const char* srcx[XL];
+  const char* srcw[WL];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int j = wave * LPW + i;
-    if (j < XBLK) {                              // activation block: XROWS rows
-      const int rl = lane / (kRowX / 16);        // row within the block
-      const int slot = lane % (kRowX / 16);
-      const int trow = XROWS * j + rl;           // row within the tile
-      const int chunk = slot ^ swz_key<kRowX>(trow);   // logical chunk landing at `slot`
-      int64_t row = m0 + trow;
-      row = row < M ? row : M - 1;
-      src[i] = reinterpret_cast<const char*>(p.X) + row * ldx + kz * kElemX + chunk * 16;
-      sstep[i] = kRowX;
-    } else {                                     // weight block: WROWS rows
-      const int rl = lane / (kRowW / 16);
-      const int slot = lane % (kRowW / 16);
-      const int trow = WROWS * (j - XBLK) + rl;
-      const int chunk = slot ^ swz_key<kRowW>(trow);
-      int64_t row = n0 + trow;
-      row = row < N ? row : N - 1;
-      src[i] = reinterpret_cast<const char*>(p.W) + row * ldw + kz * kElemW + chunk * 16;
-      sstep[i] = kRowW;
-    }
+  for (int i = 0; i < XL; ++i) {
+    const int j = wave * XL + i;
+    const int rl = lane / (kRowX / 16);          // row within the block
+    const int slot = lane % (kRowX / 16);
+    const int trow = XROWS * j + rl;             // row within the tile
+    const int chunk = slot ^ swz_key<kRowX>(trow);   // logical chunk landing at `slot`
+    int64_t row = m0 + trow;
+    row = row < M ? row : M - 1;
+    srcx[i] = reinterpret_cast<const char*>(p.X) + row * ldx + kz * kElemX + chunk * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < WL; ++i) {
+    const int j = wave * WL + i;
+    const int rl = lane / (kRowW / 16);
+    const int slot = lane % (kRowW / 16);
+    const int trow = WROWS * j + rl;
+    const int chunk = slot ^ swz_key<kRowW>(trow);
+    int64_t row = n0 + trow;
+    row = row < N ? row : N - 1;
+    srcw[i] = reinterpret_cast<const char*>(p.W) + row * ldw + kz * kElemW + chunk * 16;
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
-  auto issue = [&](int64_t kt) {
-    const uint32_t dst = lds_base + (uint32_t)(kt % STAGES) * STAGE_BYTES + wave * LPW * 1024;
+  auto issue_x = [&](int64_t kt) {
+    const uint32_t dst = lds_base + (uint32_t)(kt % STAGES) * XBYTES + wave * XL * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      dma16(src[i] + kt * sstep[i], __builtin_amdgcn_readfirstlane(dst + i * 1024));
+    for (int i = 0; i < XL; ++i)
+      dma16(srcx[i] + kt * kRowX, __builtin_amdgcn_readfirstlane(dst + i * 1024));
+  };
+  auto issue_w = [&](int64_t kt) {
+    const uint32_t dst = lds_base + WBASE + (uint32_t)(kt % STAGES) * WBYTES + wave * WL * 1024;
+#pragma unroll
+    for (int i = 0; i < WL; ++i)
+      dma16(srcw[i] + kt * kRowW, __builtin_amdgcn_readfirstlane(dst + i * 1024));
+  };
+  auto issue = [&](int64_t kt) {
+    issue_x(kt);
+    issue_w(kt);
   };
 
   using Acc = typename std::conditional<kInt, v4i, v4f>::type;
@@ -242,8 +258,8 @@ gemm_dma_kernel(GemmArgs p) {
   WFrag fa[2][FN];
   uint4 fb[2][FM];
   auto load_frags = [&](int buf, int64_t kt, int kk) {
-    const char* xs = smem + (int)(kt % STAGES) * STAGE_BYTES;
-    const char* ws = xs + XBYTES;
+    const char* xs = smem + (int)(kt % STAGES) * XBYTES;
+    const char* ws = smem + WBASE + (int)(kt % STAGES) * WBYTES;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
       const int row = wn * WN + i * 16 + frow;
@@ -398,7 +414,7 @@ gemm_dma_kernel(GemmArgs p) {
   using OutT = typename std::conditional<MODE == GemmMode::kI8toI32, int32_t, __half>::type;
   constexpr int kOut = sizeof(OutT);
   constexpr int ROWB = BN * kOut + 16;            // staged row bytes (+16: bank offset per row)
-  static_assert(BM * ROWB <= STAGES * STAGE_BYTES, "staging tile must fit in the ring");
+  static_assert(BM * ROWB <= STAGES * (XBYTES + WBYTES), "staging tile must fit in the ring");
   wait_lgkm0();
   barrier();                                      // every wave is done reading the ring
 #pragma unroll
@@ -499,6 +515,8 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 10: return launch_cfg<MODE, 2, 2, 2, 2, 4>(a, stream);  // 64x64
     case 11: return launch_cfg<MODE, 1, 4, 2, 2, 4>(a, stream);  // 32x128
     case 12: return launch_cfg<MODE, 1, 4, 2, 4, 3>(a, stream);  // 32x256
+    case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3>(a, stream);  // 256x128, 8 waves
+    case 14: return launch_cfg<MODE, 2, 4, 4, 4, 3>(a, stream);  // 128x256, 8 waves
     default: return hipErrorInvalidValue;
   }
 }

@@ -5,128 +5,25 @@
 // (fp16 Wins)", section "What changed in the computation": activation
 // equation (every call) and the weight-only listing (x_rot kept in fp16).
 //
-// Exactness.  An fp16 value is a multiple of 2^-24 below 2^16, so every
-// partial sum of the 256-point transform is a multiple of 2^-24 below 2^24:
-// 48 significand bits.  The butterflies therefore run in fp64, where they are
-// exact, and the result is rounded once (to fp32, or to fp16 through
-// round-to-odd).  gfx950 issues fp64 adds at the full vector rate, so this
-// costs the same number of VALU operations as an inexact fp32 transform.
-//
-// Layout.  A 256-group is viewed as a 16x16 matrix G[a][b] (element 16a + b)
-// and H = H16 (x) H16 (up to the 1/16), so the transform is a 16-point
-// transform along a followed by one along b.  Each group is owned by 16
-// consecutive lanes of one wavefront:
-//   1. lane a loads row a (32 contiguous bytes) and parks it in LDS;
-//   2. lane b reads column b back, transforms along a in registers (fp64);
-//   3. the columns go through an XOR-swizzled fp64 LDS transpose;
-//   4. lane c holds row c, transforms along b in registers -> 16 contiguous
-//      outputs, which become one 16-byte int8 store (or two for fp16).
-// All exchanges stay inside a wavefront; only the row maximum crosses waves.
-//
+// The rotation (exact fp64 butterflies, one rounding) and the quantisation
+// are the device functions of rotate.hpp.
+
 // Work split.  G = K/256 groups per row.  K <= 4096: a 256-thread workgroup
 // holds floor(16/G) rows.  K <= 16384: one row, 16*G threads.  Longer rows:
 // 1024 threads walk the row in chunks of 64 groups twice (maximum, then
 // quantise), recomputing the transform instead of holding the row.
 
 #include "launch.hpp"
+#include "rotate.hpp"
 
 namespace convrot {
 namespace {
-
-constexpr int kSlotBytes = 2048 + 64;  // one group: 256 doubles + bank-offset pad
-
-__device__ __forceinline__ void fwht16(double (&v)[16]) {
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if ((i & h) == 0) {
-        const double a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-    }
-  }
-}
-
-// Transform one group owned by this lane's 16-lane segment.  On return y[]
-// holds the fp64-exact outputs (16 * x_rot, i.e. before the 1/16) of row
-// `lane` of the group: elements 16*lane .. 16*lane + 15.
-__device__ __forceinline__ void rotate_group(const __half* __restrict__ src, char* slot, int lane,
-                                             double (&y)[16]) {
-  // 1. row `lane` (16 halves, 32 bytes) -> LDS staging (first 512 B of the slot)
-  const v4i* s4 = reinterpret_cast<const v4i*>(src + 16 * lane);
-  const v4i r0 = __builtin_nontemporal_load(s4);
-  const v4i r1 = __builtin_nontemporal_load(s4 + 1);
-  v4i* st = reinterpret_cast<v4i*>(slot + 32 * lane);
-  st[0] = r0;
-  st[1] = r1;
-  wave_lds_sync();
-  // 2. column `lane`: element (a, lane) for a = 0..15
-  const __half* sh = reinterpret_cast<const __half*>(slot);
-  double v[16];
-#pragma unroll
-  for (int a = 0; a < 16; ++a) v[a] = (double)__half2float(sh[16 * a + lane]);
-  wave_lds_sync();  // all staging reads done before the slot is reused below
-  fwht16(v);        // along a: v[c] = Z[c][lane]
-  // 3. transpose through LDS: Z[c][b] at row c, 16-byte chunk (b>>1)^(c&7)
-  double* sd = reinterpret_cast<double*>(slot);
-#pragma unroll
-  for (int c = 0; c < 16; ++c) sd[16 * c + 2 * ((lane >> 1) ^ (c & 7)) + (lane & 1)] = v[c];
-  wave_lds_sync();
-  const double2* rowp = reinterpret_cast<const double2*>(slot + 128 * lane);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const double2 d = rowp[q ^ (lane & 7)];
-    y[2 * q] = d.x;
-    y[2 * q + 1] = d.y;
-  }
-  wave_lds_sync();  // reads done before the next group's staging writes
-  // 4. along b
-  fwht16(y);
-}
 
 struct Split {
   int rows_per_wg;   // rows handled by one workgroup
   int gpc;           // groups per chunk (groups of one row handled at once)
   int chunks;        // chunks per row
 };
-
-// Exact-definition quantisation of 16 fp32 values with scale s (> 0):
-// q = round_half_even(fp32(v / s)).  The fast path multiplies by the
-// reciprocal; when any product lies within 3e-5 of a half-integer -- closer
-// than its possible deviation from the correctly rounded quotient -- the
-// lane falls back to IEEE division for its 16 values.
-__device__ __forceinline__ uint4 quantize16(const float (&v)[16], float s) {
-  float q[16];
-  if (s == 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = 0.0f;
-  } else {
-    const float rcp = 1.0f / s;
-    bool near_tie = false;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float t = v[i] * rcp;
-      q[i] = rintf(t);
-      near_tie |= fabsf(t - q[i]) > 0.49997f;
-    }
-    if (near_tie) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = rintf(v[i] / s);
-    }
-  }
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t b0 = (uint32_t)(int)fminf(fmaxf(q[4 * j + 0], -128.f), 127.f) & 0xffu;
-    uint32_t b1 = (uint32_t)(int)fminf(fmaxf(q[4 * j + 1], -128.f), 127.f) & 0xffu;
-    uint32_t b2 = (uint32_t)(int)fminf(fmaxf(q[4 * j + 2], -128.f), 127.f) & 0xffu;
-    uint32_t b3 = (uint32_t)(int)fminf(fmaxf(q[4 * j + 3], -128.f), 127.f) & 0xffu;
-    w[j] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 template <bool kInt8>
 __global__ void __launch_bounds__(1024)

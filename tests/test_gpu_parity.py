@@ -299,6 +299,18 @@ def test_linear_w8a8_long_rows_bitexact(M, N, K):
     assert mism == 0 and emax == 0.0
 
 
+# Assorted sizes around the tile plans: both large tiles (256x128 on 8
+# waves, 128x64), ragged M and N, K of 1 to 32 rotation groups.
+@pytest.mark.parametrize("M,N,K,bias", [(1024, 6144, 256, False), (1000, 2000, 1024, True),
+                                        (777, 300, 512, False), (129, 72, 256, True),
+                                        (600, 4100, 768, False), (1024, 256, 8192, False),
+                                        (520, 8200, 2048, True)])
+def test_linear_w8a8_assorted_shapes_bitexact(M, N, K, bias):
+    _say(f"linear w8a8 assorted M={M} N={N} K={K} bias={bias}")
+    mism, emax, rel = _w8a8_case(M, N, K, seed=M + K, bias=bias)
+    assert mism == 0 and emax == 0.0
+
+
 def test_linear_w8a8_workspace_reuse():
     # one workspace (filled with garbage first) for calls of different sizes,
     # back to back: every result bit-exact
