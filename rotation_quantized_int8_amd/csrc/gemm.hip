@@ -9,16 +9,20 @@ namespace convrot {
 
 // 256x128 tiles read half the operand bytes per output of 128x64 tiles,
 // which pays once they still give most of the 256 CUs a tile; otherwise
-// 128x64 tiles spread the work wider.  The 256x128 tile runs as 8 waves of
-// 64x64 (two per SIMD, so one wave's waits overlap the other's MFMAs).  With
-// few rows (M <= 128) the product streams the weights, and 32x64 tiles keep
-// the activation loads from being mostly padding while giving four times as
-// many workgroups.
+// 128x64 tiles spread the work wider, and when even those would leave half
+// the CUs idle, 64x64 or 32x64 tiles do.  The 256x128 tile runs as 8 waves
+// of 64x64 (two per SIMD, so one wave's waits overlap the other's MFMAs).
+// With few rows (M <= 128) the product streams the weights, and 32x64 tiles
+// keep the activation loads from being mostly padding while giving four
+// times as many workgroups.
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
   (void)mode; (void)K;
   if (M <= 128) return 9;
-  const int64_t big = ((M + 255) / 256) * ((N + 127) / 128);
-  return big >= 160 ? 13 : 8;
+  const auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (tiles(256, 128) >= 160) return 13;
+  if (tiles(128, 64) >= 128) return 8;
+  if (tiles(64, 64) >= 128) return 10;
+  return 9;
 }
 
 // W8A8 with few rows: when the 32x64 tile grid is too small to occupy the

@@ -228,13 +228,13 @@ gemm_dma_kernel(GemmArgs p) {
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
   auto issue_x = [&](int64_t kt) {
-    const uint32_t dst = lds_base + (uint32_t)(kt % STAGES) * XBYTES + wave * XL * 1024;
+    const uint32_t dst = lds_base + ((uint32_t)kt % STAGES) * XBYTES + wave * XL * 1024;
 #pragma unroll
     for (int i = 0; i < XL; ++i)
       dma16(srcx[i] + kt * kRowX, __builtin_amdgcn_readfirstlane(dst + i * 1024));
   };
   auto issue_w = [&](int64_t kt) {
-    const uint32_t dst = lds_base + WBASE + (uint32_t)(kt % STAGES) * WBYTES + wave * WL * 1024;
+    const uint32_t dst = lds_base + WBASE + ((uint32_t)kt % STAGES) * WBYTES + wave * WL * 1024;
 #pragma unroll
     for (int i = 0; i < WL; ++i)
       dma16(srcw[i] + kt * kRowW, __builtin_amdgcn_readfirstlane(dst + i * 1024));
@@ -258,8 +258,8 @@ gemm_dma_kernel(GemmArgs p) {
   WFrag fa[2][FN];
   uint4 fb[2][FM];
   auto load_frags = [&](int buf, int64_t kt, int kk) {
-    const char* xs = smem + (int)(kt % STAGES) * XBYTES;
-    const char* ws = smem + WBASE + (int)(kt % STAGES) * WBYTES;
+    const char* xs = smem + (int)((uint32_t)kt % STAGES) * XBYTES;
+    const char* ws = smem + WBASE + (int)((uint32_t)kt % STAGES) * WBYTES;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
       const int row = wn * WN + i * 16 + frow;
