@@ -30,8 +30,7 @@ __global__ void __launch_bounds__(1024)
 prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
                 int8_t* __restrict__ QX, float* __restrict__ sX, __half* __restrict__ X16) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ float gmax[64];
-  __shared__ float rowmax[16];
+  __shared__ uint32_t rowmax[16];   // per row: max |X_rot| as fp32 bits (non-negative: uint order)
 
   const int tid = threadIdx.x;
   const int slot_id = tid >> 4;     // group slot in the workgroup
@@ -47,6 +46,7 @@ prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
   double y[16];
   float f[16];
 
+  if (kInt8 && tid < 16) rowmax[tid] = 0u;
   if (!kInt8) {
     // Weight-only path: no row scale, just fp16(X H) per group.
     if (active) {
@@ -65,6 +65,7 @@ prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
     return;
   }
 
+  __syncthreads();   // rowmax cleared
   // pass 1: transform, keep the values when the row fits in one chunk, take max
   float amax = 0.0f;
   if (active) {
@@ -79,23 +80,12 @@ prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
       }
     }
   }
+  // row maximum: within each 16-lane segment, then one LDS atomic per segment
   amax = warp_max16(amax);
-  if (lane == 0) gmax[slot_id] = amax;
-  __syncthreads();
-  if (sp.rows_per_wg > 1 || sp.gpc <= 16) {
-    if (lane == 0 && gi == 0 && row_in_wg < sp.rows_per_wg) {
-      float m = 0.0f;
-      for (int j = 0; j < sp.gpc; ++j) m = fmaxf(m, gmax[row_in_wg * sp.gpc + j]);
-      rowmax[row_in_wg] = m;
-    }
-  } else if (tid < 64) {
-    float m = (tid < sp.gpc) ? gmax[tid] : 0.0f;
-    m = wave_max64(m);
-    if (tid == 0) rowmax[0] = m;
-  }
+  if (active && lane == 0) atomicMax(&rowmax[row_in_wg], __float_as_uint(amax));
   __syncthreads();
   if (!active) return;
-  const float s = rowmax[row_in_wg] / 127.0f;  // IEEE fp32 division
+  const float s = __uint_as_float(rowmax[row_in_wg]) / 127.0f;  // IEEE fp32 division
   if (slot_id == row_in_wg * sp.gpc && lane == 0) sX[row] = s;
 
   // pass 2: quantise and store
