@@ -34,7 +34,8 @@
 //
 // Epilogue: scale and bias operands are fetched at kernel entry; the finished
 // tile is converted in registers, staged through the (now idle) LDS ring and
-// written as whole 16-byte chunks of contiguous output rows.
+// written as whole 16-byte chunks of contiguous output rows with
+// non-temporal stores.
 //
 // Tile order is XCD-aware: workgroups are dispatched round-robin over the 8
 // XCDs, so the i-th workgroup on XCD x gets the i-th tile of a contiguous
@@ -469,7 +470,8 @@ gemm_dma_kernel(GemmArgs p) {
     const char* sp = smem + rl * ROWB + cc * 16;
     char* gp = outb + (m * N + n) * kOut;
     if (vec_rows && n + 16 / kOut <= N) {
-      *reinterpret_cast<uint4*>(gp) = *reinterpret_cast<const uint4*>(sp);
+      // streaming store: the output is not re-read by this kernel
+      __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(sp), reinterpret_cast<v4i*>(gp));
     } else {
 #pragma unroll
       for (int e = 0; e < 16 / kOut; ++e)
