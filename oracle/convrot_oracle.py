@@ -38,7 +38,13 @@ Readings where the pages leave a step open:
       fp32 operation with round-to-nearest-even, the scale product formed first;
   R6  W8A16: X16 = fp16(exact X H); Y = fp16(exact s_W[n] * sum_k X16 Q_W
       + lora_scale * (X D^T) U^T + bias), the LoRA term on the unrotated X and D;
-  R7  K must be a multiple of 256 and at most 131072 (so |A| < 2^31).
+  R7  K must be a multiple of 256 and at most 131072 (so |A| < 2^31);
+  R8  the W8A8 layer with its extras ([P4] "Design": bias and residual added
+      in eager's order; [P4] "What": the unmerged LoRA of the int8 linear):
+      the linear's own output is formed first -- R5's fp32 value with the bias,
+      plus, when a LoRA is given, the exact term scale * (X D^T) U^T, rounded
+      once to fp16 -- and the residual is then added as one fp16 tensor
+      addition (the exact sum of the two fp16 values, rounded once to fp16).
 """
 
 from __future__ import annotations
@@ -256,14 +262,19 @@ def int8_gemm(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
     return a.astype(np.int64)
 
 
-def epilogue_w8a8(a: np.ndarray, sx: np.ndarray, sw: np.ndarray, bias=None) -> np.ndarray:
-    """Y = fp16( fp32(A) * fp32(s_X[m] * s_W[n]) [+ bias[n]] ) (reading R5)."""
+def epilogue_w8a8_f32(a: np.ndarray, sx: np.ndarray, sw: np.ndarray, bias=None) -> np.ndarray:
+    """fp32( fp32(A) * fp32(s_X[m] * s_W[n]) [+ bias[n]] ): R5 before its fp16 cast."""
     af = np.asarray(a).astype(np.float32)
     scale = np.asarray(sx, np.float32)[:, None] * np.asarray(sw, np.float32)[None, :]
     y = af * scale
     if bias is not None:
         y = y + np.asarray(bias, np.float32)[None, :]
-    return y.astype(np.float32).astype(np.float16)
+    return y.astype(np.float32)
+
+
+def epilogue_w8a8(a: np.ndarray, sx: np.ndarray, sw: np.ndarray, bias=None) -> np.ndarray:
+    """Y = fp16( fp32(A) * fp32(s_X[m] * s_W[n]) [+ bias[n]] ) (reading R5)."""
+    return epilogue_w8a8_f32(a, sx, sw, bias).astype(np.float16)
 
 
 def linear_w8a8(x16, qw, sw, bias=None):
@@ -271,6 +282,45 @@ def linear_w8a8(x16, qw, sw, bias=None):
     qx, sx = quantize_activations(x16)
     a = int8_gemm(qx, qw)
     return epilogue_w8a8(a, sx, sw, bias), qx, sx, a
+
+
+def lora_term(x16, lora) -> np.ndarray:
+    """scale * (X down^T) up^T in float64 on the unrotated X and down ([P4] "Design").
+
+    ``lora`` is (down fp32 [R, K], up fp32 [N, R], scale).  H is symmetric and
+    orthogonal, so this equals the product of the rotated X and rotated down.
+    """
+    down, up, scale = lora
+    t = np.asarray(x16, np.float16).astype(np.float64) @ np.asarray(down, np.float32).astype(np.float64).T
+    return float(scale) * (t @ np.asarray(up, np.float32).astype(np.float64).T)
+
+
+def add_f16(a16, b16) -> np.ndarray:
+    """fp16 tensor addition: the exact sum of two fp16 values rounded once.
+
+    Two fp16 values are multiples of 2^-24 below 2^16, so their sum needs at
+    most 41 significand bits and is exact in float64; the cast to fp16 is the
+    single rounding.
+    """
+    s = np.asarray(a16, np.float16).astype(np.float64) + np.asarray(b16, np.float16).astype(np.float64)
+    return s.astype(np.float16)
+
+
+def linear_w8a8_ex(x16, qw, sw, bias=None, lora=None, residual=None) -> np.ndarray:
+    """The W8A8 linear with bias, unmerged LoRA and residual (reading R8).
+
+    Without ``lora`` and ``residual`` this is ``linear_w8a8``'s Y.  ``lora`` is
+    (down fp32 [R, K], up fp32 [N, R], scale); ``residual`` is fp16 [M, N].
+    """
+    qx, sx = quantize_activations(x16)
+    y32 = epilogue_w8a8_f32(int8_gemm(qx, qw), sx, sw, bias)
+    if lora is None:
+        y = y32.astype(np.float16)
+    else:
+        y = (y32.astype(np.float64) + lora_term(x16, lora)).astype(np.float16)
+    if residual is not None:
+        y = add_f16(y, residual)
+    return y
 
 
 # ---------------------------------------------------------------------------
@@ -293,9 +343,7 @@ def linear_w8a16(x16, qw, sw, bias=None, lora=None):
     acc = x16r @ np.asarray(qw, np.int8).astype(np.float64).T
     y = acc * np.asarray(sw, np.float32).astype(np.float64)[None, :]
     if lora is not None:
-        down, up, scale = lora
-        t = np.asarray(x16, np.float16).astype(np.float64) @ np.asarray(down, np.float32).astype(np.float64).T
-        y = y + float(scale) * (t @ np.asarray(up, np.float32).astype(np.float64).T)
+        y = y + lora_term(x16, lora)
     if bias is not None:
         y = y + np.asarray(bias, np.float32).astype(np.float64)[None, :]
     return y.astype(np.float16)

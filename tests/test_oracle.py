@@ -441,3 +441,83 @@ def test_scale_spans_the_whole_row_not_one_group():
     q, s = O.quantize_activations(x.astype(np.float16))
     assert np.all(np.abs(q[:, :256]).max(axis=1) == 127)
     assert np.all(np.abs(q[:, 256:]).max(axis=1) <= 3)
+
+
+# ------------------------------------- W8A8 with bias, LoRA and residual (R8)
+
+def _small_w8a8(seed, M=6, N=5, K=256):
+    rng = np.random.default_rng(seed)
+    x16 = rng.normal(0, 1, (M, K)).astype(np.float16)
+    w = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    qw, sw = O.quantize_weights(w)
+    bias = rng.normal(0, 0.1, N).astype(np.float32)
+    return rng, x16, qw, sw, bias
+
+
+def test_w8a8_ex_plain_is_linear_w8a8():
+    _, x16, qw, sw, bias = _small_w8a8(20)
+    for b in (None, bias):
+        a = O.linear_w8a8_ex(x16, qw, sw, bias=b)
+        want = O.linear_w8a8(x16, qw, sw, b)[0]
+        assert np.array_equal(a.view(np.uint16), want.view(np.uint16))
+
+
+def test_epilogue_f32_is_the_value_before_the_cast():
+    rng = np.random.default_rng(21)
+    a = rng.integers(-2 ** 30, 2 ** 30, (3, 4))
+    sx = (rng.random(3) * 1e-2).astype(np.float32)
+    sw = (rng.random(4) * 1e-4).astype(np.float32)
+    bias = rng.normal(0, 1, 4).astype(np.float32)
+    y = O.epilogue_w8a8_f32(a, sx, sw, bias)
+    assert y.dtype == np.float32
+    for m in range(3):
+        for n in range(4):
+            af = _rt32(Fraction(int(a[m, n])))
+            sc = _rt32(Fraction(float(sx[m])) * Fraction(float(sw[n])))
+            v = _rt32(Fraction(af) * Fraction(sc))
+            assert float(y[m, n]) == _rt32(Fraction(v) + Fraction(float(bias[n])))
+
+
+def test_w8a8_ex_residual_is_one_fp16_addition():
+    # [P4] "Design": the residual joins the layer output in eager's order, i.e.
+    # one fp16 addition of the finished fp16 output and the residual; checked
+    # against exact rational arithmetic with the exact rounding routine.
+    rng, x16, qw, sw, bias = _small_w8a8(22)
+    res = (rng.normal(0, 4, x16.shape[:1] + (qw.shape[0],))).astype(np.float16)
+    res[0, 0] = np.float16(65504.0)               # overflow of the sum must give inf or stay finite exactly
+    res[1, :] = np.float16(2.0 ** -24)            # smallest subnormal
+    y = O.linear_w8a8(x16, qw, sw, bias)[0]
+    got = O.linear_w8a8_ex(x16, qw, sw, bias=bias, residual=res)
+    for (m, n), v in np.ndenumerate(got):
+        want = _rt16(Fraction(float(y[m, n])) + Fraction(float(res[m, n])))
+        assert float(v) == want
+
+
+def test_w8a8_ex_exact_residual_cancellation():
+    _, x16, qw, sw, bias = _small_w8a8(23)
+    y = O.linear_w8a8(x16, qw, sw, bias)[0]
+    got = O.linear_w8a8_ex(x16, qw, sw, bias=bias, residual=-y)
+    assert np.all(got == 0) and not np.any(np.signbit(got[y != 0]))
+
+
+def test_w8a8_ex_lora_closed_form_unit_down_rows():
+    # With down rows e_k1, e_k2 the low-rank activation is two columns of X,
+    # so the term is scale * (X[m,k1] U[n,0] + X[m,k2] U[n,1]); the result is
+    # R5's fp32 value plus that term, rounded once to fp16 (exact rationals).
+    rng, x16, qw, sw, bias = _small_w8a8(24, M=4, N=7, K=512)
+    k1, k2 = 3, 300
+    d = np.zeros((2, 512), np.float32)
+    d[0, k1] = 1.0
+    d[1, k2] = 1.0
+    u = rng.normal(0, 0.5, (7, 2)).astype(np.float32)
+    scale = 0.75
+    qx, sx = O.quantize_activations(x16)
+    y32 = O.epilogue_w8a8_f32(O.int8_gemm(qx, qw), sx, sw, bias)
+    got = O.linear_w8a8_ex(x16, qw, sw, bias=bias, lora=(d, u, scale))
+    for (m, n), v in np.ndenumerate(got):
+        term = Fraction(scale) * (Fraction(float(x16[m, k1])) * Fraction(float(u[n, 0])) +
+                                  Fraction(float(x16[m, k2])) * Fraction(float(u[n, 1])))
+        assert float(v) == _rt16(Fraction(float(y32[m, n])) + term)
+    # and a zero up weight leaves the plain layer
+    z = O.linear_w8a8_ex(x16, qw, sw, bias=bias, lora=(d, np.zeros_like(u), scale))
+    assert np.array_equal(z, O.linear_w8a8(x16, qw, sw, bias)[0])

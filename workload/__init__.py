@@ -102,6 +102,12 @@ def make_bias(N: int, seed: int = 0, std: float = 0.1) -> torch.Tensor:
     return torch.randn((N,), generator=_gen(seed + 7), dtype=torch.float32) * std
 
 
+def make_residual(M: int, N: int, seed: int = 0, std: float = 1.0) -> torch.Tensor:
+    """A residual stream fp16 [M, N] added to the layer output (N(0, std))."""
+    r = torch.randn((M, N), generator=_gen(seed + 8), dtype=torch.float32) * std
+    return r.clamp_(-FP16_MAX, FP16_MAX).to(torch.float16)
+
+
 @dataclasses.dataclass(frozen=True)
 class Case:
     """One linear-layer problem: Y[M, N] from X[M, K] and W[N, K]."""
