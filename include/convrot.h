@@ -37,7 +37,8 @@
  *   - Sizes are int64_t.  K must be a positive multiple of 256 and at most
  *     131072 (so 127 * 127 * K < 2^31 and the int32 accumulator cannot
  *     overflow).  M == 0 or N == 0 is a valid empty call: nothing is launched.
- *   - Outputs must not overlap inputs or the workspace.
+ *   - Outputs must not overlap inputs or the workspace (one exception: the
+ *     residual of convrot_linear_w8a8_ex may be its output buffer).
  *   - Errors are returned as status codes; nothing is printed, thrown or
  *     aborted.  A non-finite input gives unspecified (but in-bounds) output.
  *   - Calls are thread-safe; calls that share an output buffer race.
@@ -72,7 +73,7 @@ typedef enum convrot_path {
   CONVROT_PATH_W8A16 = 1
 } convrot_path;
 
-/* Unmerged LoRA of the weight-only linear.  Page "[PR #249] Add an mps
+/* Unmerged LoRA of the int8 linears.  Page "[PR #249] Add an mps
  * backend: weight-only INT8 and W4A8/W6A8 linears for Apple GPUs", sections
  * "What" and "Design": lora_down [R, K], lora_up [N, R], lora_scale;
  * Y += scale * (X down^T) up^T. */
@@ -96,10 +97,10 @@ const char* convrot_status_string(int status);
 convrot_status convrot_quantize_weights(const float* W, int64_t N, int64_t K,
                                         int8_t* Q_W, float* s_W, void* stream);
 
-/* Bytes of workspace that convrot_linear_w8a8 (path = CONVROT_PATH_W8A8) or
- * convrot_linear_w8a16 (path = CONVROT_PATH_W8A16, lora_rank = 0 without
- * LoRA) need for these sizes; 0 for an empty problem, (size_t)-1 for invalid
- * sizes. */
+/* Bytes of workspace that convrot_linear_w8a8 / convrot_linear_w8a8_ex
+ * (path = CONVROT_PATH_W8A8) or convrot_linear_w8a16 (path =
+ * CONVROT_PATH_W8A16) need for these sizes, with lora_rank = 0 without LoRA;
+ * 0 for an empty problem, (size_t)-1 for invalid sizes. */
 size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_t lora_rank);
 
 /* The W8A8 ConvRot linear ("What changed in the computation", activation
@@ -111,6 +112,31 @@ convrot_status convrot_linear_w8a8(const void* X, int64_t M, int64_t K,
                                    const int8_t* Q_W, const float* s_W, int64_t N,
                                    const float* bias, void* Y,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The W8A8 ConvRot linear with the extras a model layer needs: page "[PR
+ * #249] Add an mps backend ...", section "What" (the int8 linear takes an
+ * unmerged LoRA: lora_down [R, K], lora_up [N, R], lora_scale) and section
+ * "Design" (bias and residual added in eager's order).  Computes
+ *   Y = fp16( fp32(A) * fp32(s_X[m] * s_W[n]) [+ bias[n]] [+ LoRA] )
+ *   then, with a residual, Y = fp16( Y + residual[m, n] ),
+ * where LoRA = scale * (X down^T) up^T.  Without a LoRA, Y is exact under the
+ * arithmetic contract above (the residual step is one correctly rounded fp16
+ * addition).  With a LoRA, the LoRA term is computed on fp16 MFMA with fp32
+ * accumulation (down, the low-rank activation and scale * up rounded to fp16),
+ * so Y matches the exact value within that term's rounding error.
+ *   lora:     NULL = none; otherwise rank 1 .. CONVROT_LORA_RANK_MAX and the
+ *             workspace must be sized with convrot_workspace_bytes(
+ *             CONVROT_PATH_W8A8, M, N, K, rank).
+ *   residual: NULL = none; otherwise device fp16 [M, N] (row stride N).  It
+ *             may be Y itself (in-place update: each element is read before
+ *             it is written, by the same thread) but must not otherwise
+ *             overlap Y, and must not overlap the workspace.
+ * With lora == NULL and residual == NULL this is convrot_linear_w8a8. */
+convrot_status convrot_linear_w8a8_ex(const void* X, int64_t M, int64_t K,
+                                      const int8_t* Q_W, const float* s_W, int64_t N,
+                                      const float* bias, const convrot_lora* lora,
+                                      const void* residual, void* Y,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* The weight-only (W8A16) ConvRot linear: the weight-only listing of "What
  * changed in the computation" (x_rot fp16 [M,K], qweight int8 [N,K], one

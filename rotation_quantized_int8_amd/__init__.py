@@ -7,7 +7,8 @@ There is no CPU fallback: if the library is missing or the device is not
 gfx950, the calls raise.
 
 Functions mirror the C entry points:
-  quantize_weights, linear_w8a8, linear_w8a16, act_quant, act_rotate_f16,
+  quantize_weights, linear_w8a8, linear_w8a8_ex, linear_w8a16, act_quant,
+  act_rotate_f16,
   gemm_i8_i32, gemm_i8_f16, gemm_f16, workspace_bytes.
 """
 
@@ -43,6 +44,8 @@ _SIGNATURES = {
     "convrot_workspace_bytes": (_sz, [ctypes.c_int, _i64, _i64, _i64, _i64]),
     "convrot_quantize_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "convrot_linear_w8a8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "convrot_linear_w8a8_ex": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, ctypes.POINTER(_Lora),
+                                              _vp, _vp, _vp, _sz, _vp]),
     "convrot_linear_w8a16": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp,
                                             ctypes.POINTER(_Lora), _vp, _vp, _sz, _vp]),
     "convrot_act_quant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
@@ -169,6 +172,61 @@ def linear_w8a8(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
     return y.reshape(*lead, N)
 
 
+def _lora_args(lora, N: int, K: int):
+    """(ctypes struct or None, rank, tensors to keep alive) for (down, up, scale)."""
+    if lora is None:
+        return None, 0, None
+    down, up, scale = lora
+    down = _prep(down, torch.float32, "lora_down")
+    up = _prep(up, torch.float32, "lora_up")
+    rank = down.shape[0]
+    if down.shape != (rank, K) or up.shape != (N, rank):
+        raise ValueError("lora_down must be [R, K] and lora_up [N, R]")
+    return _Lora(down.data_ptr(), up.data_ptr(), rank, float(scale)), rank, (down, up)
+
+
+def linear_w8a8_ex(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
+                   bias: Optional[torch.Tensor] = None,
+                   lora: Optional[Tuple[torch.Tensor, torch.Tensor, float]] = None,
+                   residual: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W8A8 ConvRot linear with optional bias, unmerged LoRA (down, up, scale)
+    and fp16 residual [..., N] added to the output; ``out`` (contiguous fp16
+    [..., N]) receives the result and may be ``residual`` itself."""
+    x2, lead = _flatten(_prep(x, torch.float16, "x"))
+    q_w = _prep(q_w, torch.int8, "Q_W")
+    s_w = _prep(s_w, torch.float32, "s_W")
+    bias = None if bias is None else _prep(bias, torch.float32, "bias")
+    M, K = x2.shape
+    N = q_w.shape[0]
+    if q_w.shape[1] != K:
+        raise ValueError(f"Q_W has K={q_w.shape[1]}, x has K={K}")
+    lora_struct, rank, keep = _lora_args(lora, N, K)
+    if out is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        if out.dtype != torch.float16 or not out.is_contiguous() or out.numel() != M * N:
+            raise ValueError("out must be a contiguous fp16 tensor with M * N elements")
+        y = out.view(M, N)
+    res = None
+    if residual is not None:
+        if residual.numel() != M * N:
+            raise ValueError("residual must have M * N elements")
+        if out is not None and residual.data_ptr() == out.data_ptr() and residual.is_contiguous():
+            res = y   # in-place residual update
+        else:
+            res = _prep(residual, torch.float16, "residual").view(M, N)
+    ws, nbytes = _workspace(PATH_W8A8, M, N, K, rank, x.device, workspace)
+    with torch.cuda.device(x.device):
+        _check(lib().convrot_linear_w8a8_ex(
+            _ptr(x2), M, K, _ptr(q_w), _ptr(s_w), N, _ptr(bias),
+            ctypes.byref(lora_struct) if lora_struct is not None else None,
+            _ptr(res), _ptr(y), _ptr(ws), nbytes, _stream(x2)), "convrot_linear_w8a8_ex")
+    del keep
+    return y.reshape(*lead, N)
+
+
 def linear_w8a16(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
                  bias: Optional[torch.Tensor] = None,
                  lora: Optional[Tuple[torch.Tensor, torch.Tensor, float]] = None,
@@ -182,16 +240,7 @@ def linear_w8a16(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
     N = q_w.shape[0]
     if q_w.shape[1] != K:
         raise ValueError(f"Q_W has K={q_w.shape[1]}, x has K={K}")
-    lora_struct, rank, keep = None, 0, None
-    if lora is not None:
-        down, up, scale = lora
-        down = _prep(down, torch.float32, "lora_down")
-        up = _prep(up, torch.float32, "lora_up")
-        rank = down.shape[0]
-        if down.shape != (rank, K) or up.shape != (N, rank):
-            raise ValueError("lora_down must be [R, K] and lora_up [N, R]")
-        lora_struct = _Lora(down.data_ptr(), up.data_ptr(), rank, float(scale))
-        keep = (down, up)
+    lora_struct, rank, keep = _lora_args(lora, N, K)
     y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     ws, nbytes = _workspace(PATH_W8A16, M, N, K, rank, x.device, workspace)
     with torch.cuda.device(x.device):

@@ -48,6 +48,34 @@ size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int lora_ld(int64_t rank) { return rank > 0 ? (int)((rank + 31) / 32 * 32) : 0; }
 
+// LoRA part of a workspace: T fp16 [M, t_ld], U' fp16 [N, t_ld], then (when
+// K is split) the fp32 partial sums [splits, M, t_ld].
+struct LoraWs {
+  __half* T = nullptr;
+  __half* U = nullptr;
+  float* P = nullptr;
+};
+
+size_t lora_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t rank) {
+  if (rank <= 0) return 0;
+  const size_t t_ld = (size_t)lora_ld(rank);
+  const int64_t splits = lora_splits(K);
+  return round256((size_t)M * t_ld * 2) + round256((size_t)N * t_ld * 2) +
+         (splits > 1 ? round256((size_t)splits * M * t_ld * 4) : 0);
+}
+
+LoraWs lora_ws(char* base, int64_t M, int64_t N, int64_t K, int64_t rank) {
+  LoraWs w;
+  if (rank <= 0) return w;
+  const size_t t_ld = (size_t)lora_ld(rank);
+  w.T = reinterpret_cast<__half*>(base);
+  size_t off = round256((size_t)M * t_ld * 2);
+  w.U = reinterpret_cast<__half*>(base + off);
+  off += round256((size_t)N * t_ld * 2);
+  if (lora_splits(K) > 1) w.P = reinterpret_cast<float*>(base + off);
+  return w;
+}
+
 convrot_status launched(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_LAUNCH; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -78,10 +106,9 @@ size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_
   if (path == CONVROT_PATH_W8A8) {
     const int64_t splits = w8a8_splits(M, N, K);
     return round256((size_t)M * K) + round256((size_t)M * 4) +
-           (splits > 1 ? round256((size_t)splits * M * N * 4) : 0);
+           (splits > 1 ? round256((size_t)splits * M * N * 4) : 0) + lora_ws_bytes(M, N, K, lora_rank);
   }
-  if (path == CONVROT_PATH_W8A16)
-    return round256((size_t)M * K * 2) + round256((size_t)M * lora_ld(lora_rank) * 2);
+  if (path == CONVROT_PATH_W8A16) return round256((size_t)M * K * 2) + lora_ws_bytes(M, N, K, lora_rank);
   return (size_t)-1;
 }
 
@@ -186,44 +213,98 @@ convrot_status convrot_gemm_f16(const void* X, const void* W, int64_t M, int64_t
   return launched(launch_gemm<GemmMode::kF16>(g, as_stream(stream)));
 }
 
-convrot_status convrot_linear_w8a8(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
-                                   const float* s_W, int64_t N, const float* bias, void* Y,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The W8A8 linear with its optional extras.  Workspace layout (each part
+// rounded up to 256 bytes): Q_X int8 [M, K], s_X fp32 [M], the int32
+// partials of a K split [splits, M, N] (only when split), the LoRA part
+// (only with a LoRA).
+convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
+                                const float* s_W, int64_t N, const float* bias,
+                                const convrot_lora* lora, const void* residual, void* Y,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  const int64_t rank = lora ? lora->rank : 0;
+  if (lora && (rank < 1 || rank > CONVROT_LORA_RANK_MAX)) return CONVROT_ERR_SHAPE;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
   if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
+  if (lora && (!lora->down || !lora->up)) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
-      (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
+      (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)) ||
+      (residual && !aligned16(residual)) ||
+      (lora && (!aligned16(lora->down) || !aligned16(lora->up))))
     return CONVROT_ERR_ALIGNMENT;
-  const size_t need = convrot_workspace_bytes(CONVROT_PATH_W8A8, M, N, K, 0);
+  const size_t need = convrot_workspace_bytes(CONVROT_PATH_W8A8, M, N, K, rank);
   if (!workspace || workspace_bytes < need) return CONVROT_ERR_WORKSPACE;
   const size_t yb = (size_t)M * N * 2;
-  if (overlap(Y, yb, X, (size_t)M * K * 2) || overlap(Y, yb, Q_W, (size_t)N * K) ||
-      overlap(Y, yb, s_W, (size_t)N * 4) || overlap(Y, yb, bias, bias ? (size_t)N * 4 : 0) ||
-      overlap(Y, yb, workspace, need) || overlap(workspace, need, X, (size_t)M * K * 2) ||
-      overlap(workspace, need, Q_W, (size_t)N * K) || overlap(workspace, need, s_W, (size_t)N * 4) ||
-      overlap(workspace, need, bias, bias ? (size_t)N * 4 : 0))
+  const size_t xb = (size_t)M * K * 2, qb = (size_t)N * K, sb = (size_t)N * 4;
+  const size_t bb = bias ? (size_t)N * 4 : 0, rb = residual ? yb : 0;
+  const size_t db = lora ? (size_t)rank * K * 4 : 0, ub = lora ? (size_t)N * rank * 4 : 0;
+  const void* dp = lora ? lora->down : nullptr;
+  const void* up = lora ? lora->up : nullptr;
+  // The residual may be the output buffer itself (an in-place residual
+  // update), but may not overlap it otherwise, nor the workspace.
+  if (overlap(Y, yb, X, xb) || overlap(Y, yb, Q_W, qb) || overlap(Y, yb, s_W, sb) ||
+      overlap(Y, yb, bias, bb) || overlap(Y, yb, workspace, need) || overlap(Y, yb, dp, db) ||
+      overlap(Y, yb, up, ub) || (residual != Y && overlap(Y, yb, residual, rb)) ||
+      overlap(workspace, need, X, xb) || overlap(workspace, need, Q_W, qb) ||
+      overlap(workspace, need, s_W, sb) || overlap(workspace, need, bias, bb) ||
+      overlap(workspace, need, dp, db) || overlap(workspace, need, up, ub) ||
+      overlap(workspace, need, residual, rb))
     return CONVROT_ERR_INVALID_ARG;
   if (convrot_status st = check_device()) return st;
+  hipStream_t s = as_stream(stream);
+  const int64_t splits = w8a8_splits(M, N, K);
   char* ws = reinterpret_cast<char*>(workspace);
   int8_t* QX = reinterpret_cast<int8_t*>(ws);
-  float* sX = reinterpret_cast<float*>(ws + round256((size_t)M * K));
-  hipStream_t s = as_stream(stream);
+  size_t off = round256((size_t)M * K);
+  float* sX = reinterpret_cast<float*>(ws + off);
+  off += round256((size_t)M * 4);
+  int32_t* parts = reinterpret_cast<int32_t*>(ws + off);
+  if (splits > 1) off += round256((size_t)splits * M * N * 4);
+  const LoraWs lw = lora_ws(ws + off, M, N, K, rank);
+  const int t_ld = lora_ld(rank);
+
   if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s))) return st;
+  if (lora) {
+    if (convrot_status st = launched(launch_lora_prep(X, lora->down, lora->up, lora->scale, M, N, K,
+                                                      (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
+      return st;
+  }
   GemmArgs g{};
   g.X = QX; g.W = Q_W; g.sX = sX; g.sW = s_W; g.bias = bias; g.out = Y;
+  g.R = reinterpret_cast<const __half*>(residual);
+  g.T = lw.T; g.U = lw.U; g.t_ld = t_ld;
   g.M = M; g.N = N; g.K = K;
-  const int64_t splits = w8a8_splits(M, N, K);
-  if (splits > 1) {   // few rows: int32 partials over K splits, then the scale epilogue
-    int32_t* parts = reinterpret_cast<int32_t*>(ws + round256((size_t)M * K) + round256((size_t)M * 4));
-    g.out = parts;
-    g.sX = nullptr; g.sW = nullptr; g.bias = nullptr;
-    g.kc = K / splits;
-    if (convrot_status st = launched(launch_gemm<GemmMode::kI8toI32>(g, s))) return st;
-    return launched(launch_splitk_epilogue(parts, splits, sX, s_W, bias, M, N, Y, s));
+  if (splits > 1) {   // few rows: int32 partials over K splits, then the epilogue
+    GemmArgs gi{};
+    gi.X = QX; gi.W = Q_W; gi.out = parts; gi.M = M; gi.N = N; gi.K = K; gi.kc = K / splits;
+    if (convrot_status st = launched(launch_gemm<GemmMode::kI8toI32>(gi, s))) return st;
+    return launched(launch_splitk_epilogue(parts, splits, g, s));
   }
   return launched(launch_gemm<GemmMode::kI8toF16>(g, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+convrot_status convrot_linear_w8a8(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
+                                   const float* s_W, int64_t N, const float* bias, void* Y,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_w8a8_impl(X, M, K, Q_W, s_W, N, bias, nullptr, nullptr, Y, workspace,
+                          workspace_bytes, stream);
+}
+
+convrot_status convrot_linear_w8a8_ex(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
+                                      const float* s_W, int64_t N, const float* bias,
+                                      const convrot_lora* lora, const void* residual, void* Y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_w8a8_impl(X, M, K, Q_W, s_W, N, bias, lora, residual, Y, workspace,
+                          workspace_bytes, stream);
 }
 
 convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
@@ -259,17 +340,17 @@ convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const i
   hipStream_t s = as_stream(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   void* X16 = ws;
-  __half* T = reinterpret_cast<__half*>(ws + round256((size_t)M * K * 2));
+  const LoraWs lw = lora_ws(ws + round256((size_t)M * K * 2), M, N, K, rank);
   const int t_ld = lora_ld(rank);
   if (convrot_status st = launched(launch_act_rotate_f16(X, M, K, X16, s))) return st;
   if (lora) {
-    if (convrot_status st = launched(launch_lora_down(X, lora->down, M, K, (int)rank, t_ld, T, s)))
+    if (convrot_status st = launched(launch_lora_prep(X, lora->down, lora->up, lora->scale, M, N, K,
+                                                      (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
       return st;
   }
   GemmArgs g{};
   g.X = X16; g.W = Q_W; g.sW = s_W; g.bias = bias; g.out = Y;
-  g.T = lora ? T : nullptr; g.U = lora ? lora->up : nullptr;
-  g.lora_scale = lora ? lora->scale : 0.0f; g.rank = (int)rank; g.t_ld = t_ld;
+  g.T = lw.T; g.U = lw.U; g.t_ld = t_ld;
   g.M = M; g.N = N; g.K = K;
   return launched(launch_gemm<GemmMode::kW8A16>(g, s));
 }

@@ -40,34 +40,62 @@ int64_t w8a8_splits(int64_t M, int64_t N, int64_t K) {
 
 namespace {
 
-// One thread per output: Y = fp16( fp32(sum_z A_z) * fp32(s_X * s_W) [+ bias] ),
-// the same fp32 operations in the same order as the GEMM epilogue.
-__global__ void __launch_bounds__(256)
-splitk_epilogue_kernel(const int32_t* __restrict__ parts, int64_t splits, const float* __restrict__ sX,
-                       const float* __restrict__ sW, const float* __restrict__ bias, int64_t M,
-                       int64_t N, __half* __restrict__ Y) {
-  const int64_t total = M * N;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t m = e / N, n = e - m * N;
-    int32_t a = 0;
-    for (int64_t z = 0; z < splits; ++z) a += parts[z * total + e];
-    const float sc = __fmul_rn(sX[m], sW[n]);
-    float y = __fmul_rn((float)a, sc);
-    if (bias) y = __fadd_rn(y, bias[n]);
-    Y[e] = __float2half_rn(y);
+constexpr int kEpiRows = 4;   // rows per thread of the split-K epilogue
+
+// One thread per output column n and kEpiRows rows (the loads of all its
+// rows go out together, and the column's s_W, bias and LoRA up values are
+// fetched once for them):
+//   y = fp32(sum_z A_z) * fp32(s_X * s_W) [+ bias]   (the GEMM epilogue's
+//       fp32 operations in the same order),
+//   [+ LoRA term sum_r T[m, r] U'[n, r] accumulated in fp32],
+//   Y = fp16(y) [then one fp16 addition of the residual].
+__global__ void __launch_bounds__(64)
+splitk_epilogue_kernel(const int32_t* __restrict__ parts, int64_t splits, GemmArgs p) {
+  const int64_t n = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int64_t M = p.M, N = p.N, total = M * N;
+  if (n >= N) return;
+  const int64_t m0 = (int64_t)blockIdx.y * kEpiRows;
+  int32_t a[kEpiRows];
+  float l[kEpiRows];
+#pragma unroll
+  for (int i = 0; i < kEpiRows; ++i) {
+    a[i] = 0;
+    l[i] = 0.0f;
+  }
+  for (int64_t z = 0; z < splits; ++z) {
+#pragma unroll
+    for (int i = 0; i < kEpiRows; ++i)
+      if (m0 + i < M) a[i] += parts[z * total + (m0 + i) * N + n];
+  }
+  for (int r = 0; r < p.t_ld; ++r) {
+    const float u = __half2float(p.U[n * p.t_ld + r]);
+#pragma unroll
+    for (int i = 0; i < kEpiRows; ++i)
+      if (m0 + i < M) l[i] = fmaf(__half2float(p.T[(m0 + i) * p.t_ld + r]), u, l[i]);
+  }
+  __half* Y = reinterpret_cast<__half*>(p.out);
+  const float sw = p.sW[n];
+  const float b = p.bias ? p.bias[n] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < kEpiRows; ++i) {
+    const int64_t m = m0 + i;
+    if (m >= M) break;
+    const int64_t e = m * N + n;
+    float y = __fmul_rn((float)a[i], __fmul_rn(p.sX[m], sw));
+    if (p.bias) y = __fadd_rn(y, b);
+    if (p.t_ld > 0) y = __fadd_rn(y, l[i]);
+    __half h = __float2half_rn(y);
+    if (p.R) h = __float2half_rn(__half2float(h) + __half2float(p.R[e]));
+    Y[e] = h;
   }
 }
 
 }  // namespace
 
-hipError_t launch_splitk_epilogue(const int32_t* parts, int64_t splits, const float* sX,
-                                  const float* sW, const float* bias, int64_t M, int64_t N,
-                                  void* Y, hipStream_t stream) {
-  const int64_t total = M * N;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(splitk_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, parts,
-                     splits, sX, sW, bias, M, N, reinterpret_cast<__half*>(Y));
+hipError_t launch_splitk_epilogue(const int32_t* parts, int64_t splits, const GemmArgs& a,
+                                  hipStream_t stream) {
+  const dim3 grid((unsigned)((a.N + 63) / 64), (unsigned)((a.M + kEpiRows - 1) / kEpiRows));
+  hipLaunchKernelGGL(splitk_epilogue_kernel, grid, dim3(64), 0, stream, parts, splits, a);
   return hipGetLastError();
 }
 

@@ -112,7 +112,26 @@ __device__ __forceinline__ v8h widen_i8x8(uint2 w) {
   return r;
 }
 
-template <GemmMode MODE, int WAVES_M, int WAVES_N, int FM, int FN, int STAGES, int XS>
+// MFMA operand of a LoRA product: 8 fp16 values at columns r0 + 8 (lane / 16)
+// of row `row` (clamped to rows - 1) of a [rows, t_ld] fp16 matrix.
+__device__ __forceinline__ v8h lora_frag(const __half* __restrict__ base, int64_t row, int64_t rows,
+                                         int t_ld, int r0, int lane) {
+  row = row < rows ? row : rows - 1;
+  const uint4 v = *reinterpret_cast<const uint4*>(base + row * t_ld + r0 + 8 * (lane >> 4));
+  return *reinterpret_cast<const v8h*>(&v);
+}
+
+// Eight fp16 additions, each rounded once: a + b in fp32, then to fp16.
+__device__ __forceinline__ v4i add_f16x8(v4i a, v4i b) {
+  const __half* x = reinterpret_cast<const __half*>(&a);
+  const __half* y = reinterpret_cast<const __half*>(&b);
+  __half z[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = __float2half_rn(__half2float(x[e]) + __half2float(y[e]));
+  return *reinterpret_cast<const v4i*>(z);
+}
+
+template <GemmMode MODE, int WAVES_M, int WAVES_N, int FM, int FN, int STAGES, int XS, bool EXTRA>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_dma_kernel(GemmArgs p) {
   constexpr bool kInt = (MODE == GemmMode::kI8toI32 || MODE == GemmMode::kI8toF16);
@@ -198,6 +217,20 @@ gemm_dma_kernel(GemmArgs p) {
         swv[i][r] = p.sW[nc];
         bsv[i][r] = p.bias ? p.bias[nc] : 0.0f;
       }
+  }
+
+  // LoRA operands of the first 32 rank columns (rows past M or N repeat the
+  // last row; their results are dropped)
+  constexpr bool kScaled = (MODE == GemmMode::kI8toF16 || kW16);
+  constexpr bool kLora = kScaled && EXTRA;
+  v8h lua[kLora ? FN : 1], ltb[kLora ? FM : 1];
+  if constexpr (kLora) {
+    if (p.t_ld > 0) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) lua[i] = lora_frag(p.U, n0 + wn * WN + i * 16 + (lane & 15), N, p.t_ld, 0, lane);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) ltb[j] = lora_frag(p.T, m0 + wm * WM + j * 16 + (lane & 15), M, p.t_ld, 0, lane);
+    }
   }
 
   // Per-lane direct-load sources of this wave's blocks: activation blocks
@@ -363,57 +396,92 @@ gemm_dma_kernel(GemmArgs p) {
   }
   mma(1);
 
-  // Weight-only: s_W scales the accumulators, then the LoRA product T U'^T
-  // (T = fp16(X down^T) [M, t_ld], U' = fp16(scale * up) [N, rank]) runs as
-  // extra fp16 MFMA K steps on the same accumulators.
-  if constexpr (kW16) {
+  // Unmerged LoRA: the product T U'^T (T = fp16(X down^T) [M, t_ld],
+  // U' = fp16(scale * up) [N, t_ld]) runs as extra fp16 MFMA K steps of 32
+  // rank columns on fp32 accumulators in the fragment layout.  The operands
+  // of the first step were fetched at kernel entry.
+  auto lora_mma = [&](v4f (&y)[FN][FM]) {
+    for (int r0 = 0; r0 < p.t_ld; r0 += 32) {
+      v8h ua[FN], tb[FM];
+      if (r0 == 0) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) ua[i] = lua[i];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) tb[j] = ltb[j];
+      } else {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) ua[i] = lora_frag(p.U, n0 + wn * WN + i * 16 + frow, N, p.t_ld, r0, lane);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) tb[j] = lora_frag(p.T, m0 + wm * WM + j * 16 + frow, M, p.t_ld, r0, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          y[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ua[i], tb[j], y[i][j], 0, 0, 0);
+    }
+  };
+
+  // Output geometry of the epilogue: 16-byte chunks, CPT per thread.
+  using OutT = typename std::conditional<MODE == GemmMode::kI8toI32, int32_t, __half>::type;
+  constexpr int kOut = sizeof(OutT);
+  constexpr int CPR = BN * kOut / 16;             // 16-byte chunks per tile row
+  constexpr int NTH = 64 * NW;
+  constexpr int CPT = (BM * CPR + NTH - 1) / NTH; // chunks per thread
+  const bool vec_rows = ((N * kOut) % 16) == 0;   // every output row starts 16-byte aligned
+
+  // W8A8 residual: the whole-chunk parts this thread will add are fetched now,
+  // so that their latency hides behind the epilogue arithmetic.
+  constexpr bool kRes = (MODE == GemmMode::kI8toF16) && EXTRA;
+  const __half* res = kRes ? p.R : nullptr;
+  v4i rres[kRes ? CPT : 1];
+  if constexpr (kRes) {
+    if (res && vec_rows) {
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + q * NTH;
+        const int rl = c / CPR, cc = c - rl * CPR;
+        int64_t m = m0 + rl;
+        m = m < M ? m : M - 1;
+        const int64_t n = n0 + cc * 8;
+        rres[q] = v4i{0, 0, 0, 0};
+        if (n + 8 <= N) rres[q] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(res + m * N + n));
+      }
+    }
+  }
+
+  // fp32 output tile of the scaled modes, in the fragment layout.
+  // W8A8: Y = fp32(A) * fp32(s_X * s_W) [+ bias], no contraction, then the
+  // LoRA term.  Weight-only: s_W scales the accumulators, then the LoRA term;
+  // the bias follows at the conversion to fp16.
+  v4f yf[kScaled ? FN : 1][kScaled ? FM : 1];
+  if constexpr (MODE == GemmMode::kI8toF16) {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __fmul_rn(acc[i][j][r], swv[i][r]);
-    if (p.rank > 0) {
-      for (int r0 = 0; r0 < p.t_ld; r0 += 32) {
-        v8h ua[FN], tb[FM];
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          const int64_t n = n0 + wn * WN + i * 16 + frow;
-          const int rb = r0 + 8 * fk;
-          float u[8];
-          if (n < N && rb + 8 <= p.rank && (p.rank & 3) == 0) {
-            const float4* up = reinterpret_cast<const float4*>(p.U + n * p.rank + rb);
-            const float4 u0 = up[0], u1 = up[1];
-            u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w;
-            u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) u[e] = (n < N && rb + e < p.rank) ? p.U[n * p.rank + rb + e] : 0.0f;
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ua[i][e] = (_Float16)__fmul_rn(u[e], p.lora_scale);
+        for (int r = 0; r < 4; ++r) {
+          const float sc = __fmul_rn(sxv[j], swv[i][r]);
+          float y = __fmul_rn((float)acc[i][j][r], sc);
+          if (p.bias) y = __fadd_rn(y, bsv[i][r]);
+          yf[i][j][r] = y;
         }
+  } else if constexpr (kW16) {
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const int64_t m = m0 + wm * WM + j * 16 + frow;
-          uint4 tv = make_uint4(0, 0, 0, 0);
-          if (m < M) tv = *reinterpret_cast<const uint4*>(p.T + m * p.t_ld + r0 + 8 * fk);
-          tb[j] = *reinterpret_cast<const v8h*>(&tv);
-        }
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+      for (int j = 0; j < FM; ++j)
 #pragma unroll
-          for (int j = 0; j < FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ua[i], tb[j], acc[i][j], 0, 0, 0);
-      }
-    }
+        for (int r = 0; r < 4; ++r) yf[i][j][r] = __fmul_rn(acc[i][j][r], swv[i][r]);
+  }
+  if constexpr (kLora) {
+    if (p.t_ld > 0) lora_mma(yf);
   }
 
   // ---------------------------------------------------------------- epilogue
   // The finished tile goes through LDS (the ring is free now) so that global
   // stores are whole 16-byte chunks of contiguous output rows.
-  using OutT = typename std::conditional<MODE == GemmMode::kI8toI32, int32_t, __half>::type;
-  constexpr int kOut = sizeof(OutT);
   constexpr int ROWB = BN * kOut + 16;            // staged row bytes (+16: bank offset per row)
   static_assert(BM * ROWB <= STAGES * (XBYTES + WBYTES), "staging tile must fit in the ring");
   wait_lgkm0();
@@ -431,17 +499,11 @@ gemm_dma_kernel(GemmArgs p) {
         __half h[4];
         if constexpr (MODE == GemmMode::kI8toF16) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // Y = fp16( fp32(A) * fp32(s_X * s_W) [+ bias] ), no contraction
-            const float sc = __fmul_rn(sxv[j], swv[i][r]);
-            float y = __fmul_rn((float)acc[i][j][r], sc);
-            if (p.bias) y = __fadd_rn(y, bsv[i][r]);
-            h[r] = __float2half_rn(y);
-          }
+          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(yf[i][j][r]);
         } else if constexpr (kW16) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float y = acc[i][j][r];
+            float y = yf[i][j][r];
             if (p.bias) y = __fadd_rn(y, bsv[i][r]);
             h[r] = __float2half_rn(y);
           }
@@ -457,12 +519,16 @@ gemm_dma_kernel(GemmArgs p) {
     }
   }
   barrier();
-  constexpr int CPR = BN * kOut / 16;             // 16-byte chunks per tile row
-  constexpr int NTH = 64 * NW;
-  const bool vec_rows = ((N * kOut) % 16) == 0;   // every output row starts 16-byte aligned
   char* outb = reinterpret_cast<char*>(p.out) + (int64_t)blockIdx.y * M * N * kOut;
-#pragma unroll 4
-  for (int c = tid; c < BM * CPR; c += NTH) {
+  // The residual is one fp16 addition to the finished fp16 output (the fp32
+  // sum of two fp16 values rounded to fp16 is their correctly rounded fp16
+  // sum: fp32 carries more than twice fp16's precision).  Each element's
+  // residual is read by the thread that writes that element, before the
+  // write, so the residual may be the output buffer itself.
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int c = tid + q * NTH;
+    if (c >= BM * CPR) break;
     const int rl = c / CPR, cc = c - rl * CPR;
     const int64_t m = m0 + rl;
     if (m >= M) continue;
@@ -470,23 +536,33 @@ gemm_dma_kernel(GemmArgs p) {
     const char* sp = smem + rl * ROWB + cc * 16;
     char* gp = outb + (m * N + n) * kOut;
     if (vec_rows && n + 16 / kOut <= N) {
+      v4i v = *reinterpret_cast<const v4i*>(sp);
+      if constexpr (kRes) {
+        if (res) v = add_f16x8(v, rres[q]);
+      }
       // streaming store: the output is not re-read by this kernel
-      __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(sp), reinterpret_cast<v4i*>(gp));
+      __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(gp));
     } else {
 #pragma unroll
-      for (int e = 0; e < 16 / kOut; ++e)
-        if (n + e < N) reinterpret_cast<OutT*>(gp)[e] = reinterpret_cast<const OutT*>(sp)[e];
+      for (int e = 0; e < 16 / kOut; ++e) {
+        if (n + e >= N) continue;
+        OutT o = reinterpret_cast<const OutT*>(sp)[e];
+        if constexpr (kRes) {
+          if (res) o = __float2half_rn(__half2float(o) + __half2float(res[m * N + n + e]));
+        }
+        reinterpret_cast<OutT*>(gp)[e] = o;
+      }
     }
   }
 }
 
-template <GemmMode MODE, int WAM, int WAN, int FM, int FN, int ST, int XS = 128>
+template <GemmMode MODE, int WAM, int WAN, int FM, int FN, int ST, bool EXTRA = false, int XS = 128>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int BM = 16 * FM * WAM, BN = 16 * FN * WAN;
   constexpr int kRowW = MODE == GemmMode::kW8A16 ? XS / 2 : XS;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const size_t lds = (size_t)ST * ((size_t)BM * XS + (size_t)BN * kRowW);
-  auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST, XS>;
+  auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST, XS, EXTRA>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -501,8 +577,22 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 
 // Configuration table: id -> (wave grid, fragments per wave, pipeline depth).
 // Output tile = (16 FM WAVES_M) x (16 FN WAVES_N) in (M, N).
+// A residual or a LoRA selects the kernels compiled with those epilogue
+// steps (only for the tile configurations the library dispatches to), so
+// the plain kernels carry none of their registers or code.
 template <GemmMode MODE>
 hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
+  if constexpr (MODE == GemmMode::kI8toF16 || MODE == GemmMode::kW8A16) {
+    if (a.R || a.t_ld > 0) {
+      switch (cfg) {
+        case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4, true>(a, stream);
+        case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4, true>(a, stream);
+        case 10: return launch_cfg<MODE, 2, 2, 2, 2, 4, true>(a, stream);
+        case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3, true>(a, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   switch (cfg) {
     case 0: return launch_cfg<MODE, 2, 2, 4, 4, 3>(a, stream);   // 128x128
     case 1: return launch_cfg<MODE, 2, 2, 4, 4, 4>(a, stream);   // 128x128, 4 stages

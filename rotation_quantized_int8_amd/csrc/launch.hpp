@@ -13,11 +13,10 @@ struct GemmArgs {
   const float* sX;      // [M]   (kI8toF16)
   const float* sW;      // [N]   (kI8toF16, kW8A16)
   const float* bias;    // [N] or null
-  const __half* T;      // [M, t_ld] fp16 LoRA activation (kW8A16, may be null)
-  const float* U;       // [N, rank] fp32 LoRA up (kW8A16, may be null)
-  float lora_scale;
-  int rank;             // LoRA rank (0 = none)
-  int t_ld;             // row stride of T (rank rounded up to 32)
+  const __half* R;      // [M, N] fp16 residual added to the fp16 output (kI8toF16), or null
+  const __half* T;      // [M, t_ld] fp16 LoRA activation X down^T (kI8toF16, kW8A16)
+  const __half* U;      // [N, t_ld] fp16 LoRA up weight U' = fp16(scale * up), zero past the rank
+  int t_ld;             // LoRA rank rounded up to 32 (0 = no LoRA)
   void* out;            // [M, N] int32 or fp16; with kc: [K / kc, M, N] int32 partials
   int64_t M, N, K;
   int64_t kc;           // 0, or K per split (kI8toI32 only; a multiple of 256 dividing K)
@@ -34,10 +33,11 @@ int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K);
 
 // Split-K plan of the W8A8 linear: number of K splits (1 = none) for a size.
 int64_t w8a8_splits(int64_t M, int64_t N, int64_t K);
-// Y = fp16(fp32(sum_z A_z) * fp32(s_X s_W) [+ bias]) from the int32 partials.
-hipError_t launch_splitk_epilogue(const int32_t* parts, int64_t splits, const float* sX,
-                                  const float* sW, const float* bias, int64_t M, int64_t N,
-                                  void* Y, hipStream_t stream);
+// Y = fp16(fp32(sum_z A_z) * fp32(s_X s_W) [+ bias]) from the int32 partials,
+// then the optional LoRA term (a.T, a.U, a.t_ld) before the fp16 rounding and
+// the optional residual a.R after it.
+hipError_t launch_splitk_epilogue(const int32_t* parts, int64_t splits, const GemmArgs& a,
+                                  hipStream_t stream);
 
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* QW, float* sW,
                                    hipStream_t stream);
@@ -45,7 +45,14 @@ hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, flo
                             hipStream_t stream);
 hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
                                  hipStream_t stream);
-hipError_t launch_lora_down(const void* X, const float* D, int64_t M, int64_t K, int rank,
-                            int t_ld, void* T, hipStream_t stream);
+
+// LoRA operands of the GEMM epilogue: T fp16 [M, t_ld] = X down^T and
+// U' fp16 [N, t_ld] = fp16(scale * up) (columns past the rank zero).  K is
+// split into lora_splits(K) ranges; with more than one, the fp32 partial sums
+// P [splits, M, t_ld] go through the workspace.
+int64_t lora_splits(int64_t K);
+hipError_t launch_lora_prep(const void* X, const float* down, const float* up, float scale, int64_t M,
+                            int64_t N, int64_t K, int rank, int t_ld, float* P, __half* T, __half* U,
+                            hipStream_t stream);
 
 }  // namespace convrot

@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = cr.header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 12
     for name in declared:
         assert hasattr(L, name), name
     assert set(declared) == set(cr._SIGNATURES)
@@ -43,6 +43,11 @@ def test_workspace_bytes(L):
     assert L.convrot_workspace_bytes(0, 0, 5, 256, 0) == 0
     # few rows and a small tile grid: room for 8 K-split int32 partials
     assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 0) == 16 * 8192 + 256 + 8 * 16 * 2048 * 4
+    # a LoRA adds its fp16 low-rank activation [M, rank rounded up to 32] and,
+    # when K spans several 256-column chunks, fp32 partial sums per K range
+    assert L.convrot_workspace_bytes(0, 3, 5, 256, 17) == 768 + 256 + 256
+    assert L.convrot_workspace_bytes(0, 1024, 2048, 2048, 64) == \
+        1024 * 2048 + 4096 + 1024 * 64 * 2 + 8 * 1024 * 64 * 4
     bad = ctypes.c_size_t(-1).value
     assert L.convrot_workspace_bytes(0, 4, 4, 255, 0) == bad
     assert L.convrot_workspace_bytes(0, 4, 4, 131072 + 256, 0) == bad
@@ -81,6 +86,35 @@ def test_linear_w8a8_argument_errors(L):
     assert f(P, 4, 256, Q, R, 8, None, P + 16, S + 4096, ws, None) == INVALID
     assert f(P, 4, 256, Q, R, 8, None, S, S, ws, None) == INVALID
     assert f(P, 4, 256, Q, R, 8, None, S, P, ws, None) == INVALID
+
+
+def test_linear_w8a8_ex_argument_errors(L):
+    f = L.convrot_linear_w8a8_ex
+    ws = L.convrot_workspace_bytes(0, 4, 8, 256, 0)
+    Y, W = S, S + 4096
+    # (no call here may pass every host check: with a GPU present it would
+    # launch kernels on these fake addresses)
+    assert f(None, 0, 256, None, None, 8, None, None, None, None, None, 0, None) == OK
+    # residual: alignment, partial overlap with Y, overlap with the workspace
+    assert f(P, 4, 256, Q, R, 8, None, None, Y + 8, Y, W, ws, None) == ALIGN
+    assert f(P, 4, 256, Q, R, 8, None, None, Y + 16, Y, W, ws, None) == INVALID
+    assert f(P, 4, 256, Q, R, 8, None, None, W + 256, Y, W, ws, None) == INVALID
+    # LoRA: rank, null factors, alignment, workspace sized for the rank
+    lora = cr._Lora(P + 65536, Q + 65536, 0, 1.0)
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), None, Y, W, ws, None) == SHAPE
+    lora.rank = 65
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), None, Y, W, ws, None) == SHAPE
+    lora.rank, lora.up = 4, None
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), None, Y, W, ws, None) == INVALID
+    lora.up = Q + 65536 + 4
+    wsl = L.convrot_workspace_bytes(0, 4, 8, 256, 4)
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), None, Y, W, wsl, None) == ALIGN
+    lora.up = Q + 65536
+    assert wsl > ws
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), None, Y, W, ws, None) == WORKSPACE
+    # output overlapping a LoRA factor
+    lora.down = Y + 256
+    assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), None, Y, W, wsl, None) == INVALID
 
 
 def test_linear_w8a16_argument_errors(L):

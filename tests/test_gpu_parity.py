@@ -368,13 +368,120 @@ def test_linear_w8a8_graph_replays_match_eager():
     _say("  4 replays x 3 calls equal to the eager result")
 
 
-# ------------------------------------------------ weight-only W8A16 (a6, a7)
+# ------------------------------ W8A8 with bias, unmerged LoRA and residual
 
 def _ulp16(y):
     a = np.abs(y.astype(np.float64))
     e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
     return np.exp2(e - 10)
 
+
+def _w8a8_ex_case(M, N, K, seed, bias=False, rank=0, residual=True, in_place=False, up_zero=False):
+    """Runs the GPU and the oracle on one seeded case; returns (Y_gpu, Y_oracle, tolerance)."""
+    x = wl.make_activations(M, K, seed=seed)
+    w = wl.make_weights(N, K, seed=seed)
+    qw, sw = O.quantize_weights(w.numpy())
+    b = wl.make_bias(N, seed=seed) if bias else None
+    r = wl.make_residual(M, N, seed=seed) if residual else None
+    lora = None
+    if rank:
+        d, u = wl.make_lora(N, K, rank=rank, seed=seed)
+        if up_zero:
+            u = torch.zeros_like(u)
+        lora = (d, u, 0.5)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    dlora = None if lora is None else (lora[0].to(DEV), lora[1].to(DEV), lora[2])
+    db = None if b is None else b.to(DEV)
+    if in_place:
+        buf = r.to(DEV).clone()
+        yt = cr.linear_w8a8_ex(x.to(DEV), t(qw), t(sw), bias=db, lora=dlora, residual=buf, out=buf)
+        assert yt.data_ptr() == buf.data_ptr()
+    else:
+        yt = cr.linear_w8a8_ex(x.to(DEV), t(qw), t(sw), bias=db, lora=dlora,
+                               residual=None if r is None else r.to(DEV))
+    yg = _np(yt)
+    olora = None if lora is None else (lora[0].numpy(), lora[1].numpy(), lora[2])
+    ob = None if b is None else b.numpy()
+    yo = O.linear_w8a8_ex(x.numpy(), qw, sw, bias=ob, lora=olora, residual=None if r is None else r.numpy())
+    tol = np.zeros(yo.shape)
+    if lora is not None:
+        # the LoRA term is fp16 MFMA work (down, T and scale * up rounded to
+        # fp16, fp32 sums): bounded by 2^-9 of the sum of its magnitudes; one
+        # fp16 ulp before the residual step and one after it cover the roundings
+        pre = O.linear_w8a8_ex(x.numpy(), qw, sw, bias=ob, lora=olora)
+        tt = np.abs(x.numpy().astype(np.float64) @ olora[0].astype(np.float64).T)
+        s_lora = abs(olora[2]) * (tt @ np.abs(olora[1].astype(np.float64)).T)
+        tol = _ulp16(pre) + (_ulp16(yo) if r is not None else 0.0) + 2.0 ** -9 * s_lora
+    return yg, yo, tol
+
+
+@pytest.mark.parametrize("M,N,K,bias", [(64, 256, 256, False), (300, 203, 768, True),
+                                        (1024, 2048, 2048, True), (16, 2048, 8192, True),
+                                        (5, 200, 4096, False), (1024, 6144, 256, True),
+                                        (129, 72, 256, True)])
+def test_linear_w8a8_ex_bias_residual_bitexact(M, N, K, bias):
+    # no LoRA: the residual step is one correctly rounded fp16 addition, so
+    # the whole result is exact (few-row shapes take the K-split path)
+    _say(f"linear w8a8_ex bias+residual M={M} N={N} K={K} bias={bias}")
+    yg, yo, _ = _w8a8_ex_case(M, N, K, seed=M + 3 * N, bias=bias)
+    mism = int((yg.view(np.uint16) != yo.view(np.uint16)).sum())
+    _say(f"  mismatches {mism} / {yo.size}")
+    assert mism == 0
+
+
+@pytest.mark.parametrize("M,N,K,rank", [(300, 203, 768, 0), (16, 2048, 8192, 0), (1024, 2048, 2048, 0),
+                                        (64, 256, 256, 32), (16, 2048, 8192, 32)])
+def test_linear_w8a8_ex_in_place_residual(M, N, K, rank):
+    _say(f"linear w8a8_ex in-place residual M={M} N={N} K={K} rank={rank}")
+    yg, yo, tol = _w8a8_ex_case(M, N, K, seed=M + N + rank, bias=True, rank=rank, in_place=True)
+    if rank == 0:
+        assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+    else:
+        d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
+        assert int((d > tol).sum()) == 0
+
+
+@pytest.mark.parametrize("M,N,K,rank,bias,residual", [(64, 256, 256, 32, True, True),
+                                                      (300, 203, 768, 17, True, True),
+                                                      (1, 8, 512, 64, False, True),
+                                                      (1024, 2048, 2048, 32, True, True),
+                                                      (1024, 6144, 256, 32, False, False),
+                                                      (16, 2048, 8192, 32, True, True),
+                                                      (5, 200, 4096, 3, False, False)])
+def test_linear_w8a8_ex_lora_within_tolerance(M, N, K, rank, bias, residual):
+    _say(f"linear w8a8_ex LoRA M={M} N={N} K={K} rank={rank} bias={bias} residual={residual}")
+    yg, yo, tol = _w8a8_ex_case(M, N, K, seed=M + rank, bias=bias, rank=rank, residual=residual)
+    d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
+    viol = int((d > tol).sum())
+    rel = float(np.linalg.norm(d) / np.linalg.norm(yo.astype(np.float64)))
+    exact = int((yg.view(np.uint16) == yo.view(np.uint16)).sum())
+    _say(f"  violations {viol}, max |dY|/tol {float((d / tol).max()):.3f}, bit-equal {exact}/{yo.size}, "
+         f"rel. Frobenius {rel:.2e}")
+    assert viol == 0 and rel <= 1e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (16, 2048, 8192), (300, 203, 768)])
+def test_linear_w8a8_ex_zero_up_is_exact(M, N, K):
+    # a LoRA whose up weight is zero adds exact zeros: the result is the exact
+    # bias + residual layer, bit for bit, on both the GEMM and K-split paths
+    _say(f"linear w8a8_ex zero-up LoRA M={M} N={N} K={K}")
+    yg, _, _ = _w8a8_ex_case(M, N, K, seed=7 * M, bias=True, rank=32, up_zero=True)
+    _, yo, _ = _w8a8_ex_case(M, N, K, seed=7 * M, bias=True)
+    assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+
+
+def test_linear_w8a8_ex_without_extras_equals_linear_w8a8():
+    _say("linear w8a8_ex without extras == linear w8a8")
+    for (M, N, K) in ((300, 203, 768), (16, 2048, 8192)):
+        x = wl.make_activations(M, K, seed=41).to(DEV)
+        qw, sw = cr.quantize_weights(wl.make_weights(N, K, seed=41).to(DEV))
+        b = wl.make_bias(N, seed=41).to(DEV)
+        a = cr.linear_w8a8(x, qw, sw, b)
+        e = cr.linear_w8a8_ex(x, qw, sw, bias=b)
+        assert torch.equal(a.view(torch.int16), e.view(torch.int16))
+
+
+# ------------------------------------------------ weight-only W8A16 (a6, a7)
 
 def _w8a16_case(M, N, K, rank=0, bias=False, seed=0):
     x = wl.make_activations(M, K, seed=seed)
