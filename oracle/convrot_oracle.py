@@ -44,7 +44,11 @@ Readings where the pages leave a step open:
       the linear's own output is formed first -- R5's fp32 value with the bias,
       plus, when a LoRA is given, the exact term scale * (X D^T) U^T, rounded
       once to fp16 -- and the residual is then added as one fp16 tensor
-      addition (the exact sum of the two fp16 values, rounded once to fp16).
+      addition (the exact sum of the two fp16 values, rounded once to fp16);
+  R10 the dequantise-every-call baseline ([P1] "What changed in the
+      computation": the earlier patch turned Q_W (.) s_W back into fp16,
+      un-rotated it and ran the plain X W^T): W_deq = fp16(exact (Q_W (.) s_W) H),
+      one rounding (H is its own inverse), then Y = fp16(exact X W_deq^T + bias).
 """
 
 from __future__ import annotations
@@ -344,6 +348,30 @@ def linear_w8a16(x16, qw, sw, bias=None, lora=None):
     y = acc * np.asarray(sw, np.float32).astype(np.float64)[None, :]
     if lora is not None:
         y = y + lora_term(x16, lora)
+    if bias is not None:
+        y = y + np.asarray(bias, np.float32).astype(np.float64)[None, :]
+    return y.astype(np.float16)
+
+
+def dequantize_weights(qw, sw) -> np.ndarray:
+    """W_deq = fp16( (Q_W (.) s_W) H ) per 256-group, rounded once (reading R10).
+
+    Exactness: the group sum is s_W[n] / 16 times an integer of magnitude at
+    most 256 * 128 = 2^15, so the float64 product of that integer with the
+    fp32 scale has at most 15 + 24 bits and is exact; the cast to fp16 is the
+    single rounding.
+    """
+    q = np.asarray(qw, np.int8).astype(np.int64)
+    N, K = q.shape
+    _check_k(K)
+    t = (q.reshape(N, K // GROUP, GROUP) @ hadamard256_pm1()).reshape(N, K)   # exact integers
+    w = t.astype(np.float64) * (np.asarray(sw, np.float32).astype(np.float64)[:, None] / 16.0)
+    return w.astype(np.float16)
+
+
+def linear_dequant(x16, qw, sw, bias=None) -> np.ndarray:
+    """Dequantise-every-call baseline: fp16( X W_deq^T [+ bias] ), the sum in float64."""
+    y = np.asarray(x16, np.float16).astype(np.float64) @ dequantize_weights(qw, sw).astype(np.float64).T
     if bias is not None:
         y = y + np.asarray(bias, np.float32).astype(np.float64)[None, :]
     return y.astype(np.float16)

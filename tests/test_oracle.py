@@ -521,3 +521,62 @@ def test_w8a8_ex_lora_closed_form_unit_down_rows():
     # and a zero up weight leaves the plain layer
     z = O.linear_w8a8_ex(x16, qw, sw, bias=bias, lora=(d, np.zeros_like(u), scale))
     assert np.array_equal(z, O.linear_w8a8(x16, qw, sw, bias)[0])
+
+
+# ------------------------------------- dequantise-every-call baseline (R10)
+
+def test_dequantize_matches_exact_rationals():
+    # fp16 of the exact un-rotated dequantised weight, element by element with
+    # rational arithmetic and the explicit +-1 matrix
+    rng = np.random.default_rng(30)
+    q = rng.integers(-127, 128, (3, 512)).astype(np.int8)
+    s = (rng.random(3) * 1e-3).astype(np.float32)
+    s[2] = np.float32(2.0 ** -130)      # subnormal scale: results underflow in fp16
+    w = O.dequantize_weights(q, s)
+    hpm = O.hadamard256_pm1()
+    for n in range(3):
+        for k in (0, 1, 255, 256, 300, 511):
+            g, c = divmod(k, 256)
+            tot = sum(int(q[n, 256 * g + j]) * int(hpm[j, c]) for j in range(256))
+            exact = Fraction(tot) * Fraction(float(s[n])) / 16
+            assert float(w[n, k]) == _rt16(exact)
+
+
+def test_dequantize_inverts_quantization_within_its_error():
+    # H is orthogonal: per group the L2 distance to W is the rotated-domain
+    # quantisation error, at most sqrt(256) * s_W / 2, plus fp16 rounding
+    rng = np.random.default_rng(31)
+    w = rng.normal(0, 0.02, (8, 768)).astype(np.float32)
+    qw, sw = O.quantize_weights(w)
+    wd = O.dequantize_weights(qw, sw).astype(np.float64)
+    for n in range(8):
+        for g in range(3):
+            d = wd[n, 256 * g:256 * (g + 1)] - w[n, 256 * g:256 * (g + 1)]
+            bound = 16 * float(sw[n]) / 2 + 16 * 2.0 ** -11 * np.abs(w[n]).max()
+            assert np.linalg.norm(d) <= bound
+
+
+def test_dequantize_of_scaled_hadamard_row_is_one_hot():
+    # a weight row that is 127 * (row j of the +-1 matrix) with scale 1/127
+    # un-rotates to 16 e_j (H = Hpm / 16 and Hpm Hpm = 256 I)
+    hpm = O.hadamard256_pm1()
+    q = (127 * hpm[[5, 200]]).astype(np.int8)
+    s = np.full(2, 1 / 127, np.float32)
+    w = O.dequantize_weights(q, s).astype(np.float64)
+    exp = np.zeros((2, 256))
+    exp[0, 5] = exp[1, 200] = 16 * 127 * float(np.float32(1 / 127))
+    assert np.array_equal(w, exp.astype(np.float16).astype(np.float64))
+
+
+def test_linear_dequant_is_fp16_matmul_of_the_dequantised_weight():
+    rng = np.random.default_rng(32)
+    x16 = rng.integers(-4, 5, (5, 256)).astype(np.float16)
+    q = rng.integers(-127, 128, (6, 256)).astype(np.int8)
+    s = np.full(6, 2.0 ** -10, np.float32)
+    b = rng.integers(-3, 4, 6).astype(np.float32)
+    wd = O.dequantize_weights(q, s)
+    y = O.linear_dequant(x16, q, s, b)
+    for m in range(5):
+        for n in range(6):
+            exact = sum(Fraction(float(x16[m, k])) * Fraction(float(wd[n, k])) for k in range(256)) + Fraction(float(b[n]))
+            assert float(y[m, n]) == _rt16(exact)
