@@ -70,7 +70,8 @@ typedef enum convrot_status {
 
 typedef enum convrot_path {
   CONVROT_PATH_W8A8 = 0,
-  CONVROT_PATH_W8A16 = 1
+  CONVROT_PATH_W8A16 = 1,
+  CONVROT_PATH_DEQUANT = 2
 } convrot_path;
 
 /* Unmerged LoRA of the int8 linears.  Page "[PR #249] Add an mps
@@ -98,9 +99,10 @@ convrot_status convrot_quantize_weights(const float* W, int64_t N, int64_t K,
                                         int8_t* Q_W, float* s_W, void* stream);
 
 /* Bytes of workspace that convrot_linear_w8a8 / convrot_linear_w8a8_ex
- * (path = CONVROT_PATH_W8A8) or convrot_linear_w8a16 (path =
- * CONVROT_PATH_W8A16) need for these sizes, with lora_rank = 0 without LoRA;
- * 0 for an empty problem, (size_t)-1 for invalid sizes. */
+ * (path = CONVROT_PATH_W8A8), convrot_linear_w8a16 (path =
+ * CONVROT_PATH_W8A16) or convrot_linear_dequant (path =
+ * CONVROT_PATH_DEQUANT, lora_rank 0) need for these sizes, with lora_rank = 0
+ * without LoRA; 0 for an empty problem, (size_t)-1 for invalid sizes. */
 size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_t lora_rank);
 
 /* The W8A8 ConvRot linear ("What changed in the computation", activation
@@ -150,7 +152,25 @@ convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K,
                                     const float* bias, const convrot_lora* lora, void* Y,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* The dequantise-every-call baseline the pages compare against (page
+ * "INT8ConvRot GEMM vs fp16 on M1 Max ...", section "What changed in the
+ * computation": the int8 weights and their scale are turned back into fp16
+ * and un-rotated on every call, then a plain fp16 X W^T runs; its three-way
+ * table times this path).  W_deq = fp16((Q_W (.) s_W) H) goes to the workspace
+ * (fp16 [N, K], exact before its one rounding); then Y fp16 [M, N] =
+ * fp16(X W_deq^T [+ bias]) on fp16 MFMA with fp32 accumulation, so Y matches
+ * the exact value within accumulation error, not bit for bit. */
+convrot_status convrot_linear_dequant(const void* X, int64_t M, int64_t K,
+                                      const int8_t* Q_W, const float* s_W, int64_t N,
+                                      const float* bias, void* Y,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- stages (exported for parity tests and per-kernel measurement) ---- */
+
+/* The baseline's weight step alone: Q_W int8 [N, K], s_W fp32 [N] ->
+ * W16 fp16 [N, K] = fp16((Q_W (.) s_W) H), correctly rounded. */
+convrot_status convrot_dequantize_weights(const int8_t* Q_W, const float* s_W, int64_t N, int64_t K,
+                                          void* W16, void* stream);
 
 /* Prologue alone: X fp16 [M, K] -> Q_X int8 [M, K], s_X fp32 [M]. */
 convrot_status convrot_act_quant(const void* X, int64_t M, int64_t K,

@@ -7,8 +7,8 @@ There is no CPU fallback: if the library is missing or the device is not
 gfx950, the calls raise.
 
 Functions mirror the C entry points:
-  quantize_weights, linear_w8a8, linear_w8a8_ex, linear_w8a16, act_quant,
-  act_rotate_f16,
+  quantize_weights, linear_w8a8, linear_w8a8_ex, linear_w8a16, linear_dequant,
+  dequantize_weights, act_quant, act_rotate_f16,
   gemm_i8_i32, gemm_i8_f16, gemm_f16, workspace_bytes.
 """
 
@@ -27,6 +27,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG_DIR), "include", "convrot.h")
 
 PATH_W8A8 = 0
 PATH_W8A16 = 1
+PATH_DEQUANT = 2
 GROUP = 256
 K_MAX = 131072
 LORA_RANK_MAX = 64
@@ -48,6 +49,8 @@ _SIGNATURES = {
                                               _vp, _vp, _vp, _sz, _vp]),
     "convrot_linear_w8a16": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp,
                                             ctypes.POINTER(_Lora), _vp, _vp, _sz, _vp]),
+    "convrot_linear_dequant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "convrot_dequantize_weights": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "convrot_act_quant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "convrot_act_rotate_f16": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "convrot_gemm_i8_i32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -249,6 +252,39 @@ def linear_w8a16(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
             ctypes.byref(lora_struct) if lora_struct is not None else None,
             _ptr(y), _ptr(ws), nbytes, _stream(x2)), "convrot_linear_w8a16")
     del keep
+    return y.reshape(*lead, N)
+
+
+def dequantize_weights(q_w: torch.Tensor, s_w: torch.Tensor) -> torch.Tensor:
+    """Q_W int8 [N, K], s_W fp32 [N] -> fp16((Q_W * s_W) H) [N, K] (un-rotated)."""
+    q_w = _prep(q_w, torch.int8, "Q_W")
+    s_w = _prep(s_w, torch.float32, "s_W")
+    N, K = q_w.shape
+    out = torch.empty((N, K), dtype=torch.float16, device=q_w.device)
+    with torch.cuda.device(q_w.device):
+        _check(lib().convrot_dequantize_weights(_ptr(q_w), _ptr(s_w), N, K, _ptr(out), _stream(q_w)),
+               "convrot_dequantize_weights")
+    return out
+
+
+def linear_dequant(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
+                   bias: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dequantise-every-call baseline: fp16(x W_deq^T [+ bias]), W_deq rebuilt each call."""
+    x2, lead = _flatten(_prep(x, torch.float16, "x"))
+    q_w = _prep(q_w, torch.int8, "Q_W")
+    s_w = _prep(s_w, torch.float32, "s_W")
+    bias = None if bias is None else _prep(bias, torch.float32, "bias")
+    M, K = x2.shape
+    N = q_w.shape[0]
+    if q_w.shape[1] != K:
+        raise ValueError(f"Q_W has K={q_w.shape[1]}, x has K={K}")
+    y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    ws, nbytes = _workspace(PATH_DEQUANT, M, N, K, 0, x.device, workspace)
+    with torch.cuda.device(x.device):
+        _check(lib().convrot_linear_dequant(_ptr(x2), M, K, _ptr(q_w), _ptr(s_w), N, _ptr(bias),
+                                            _ptr(y), _ptr(ws), nbytes, _stream(x2)),
+               "convrot_linear_dequant")
     return y.reshape(*lead, N)
 
 

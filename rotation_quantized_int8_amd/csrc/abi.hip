@@ -109,6 +109,7 @@ size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_
            (splits > 1 ? round256((size_t)splits * M * N * 4) : 0) + lora_ws_bytes(M, N, K, lora_rank);
   }
   if (path == CONVROT_PATH_W8A16) return round256((size_t)M * K * 2) + lora_ws_bytes(M, N, K, lora_rank);
+  if (path == CONVROT_PATH_DEQUANT) return lora_rank == 0 ? round256((size_t)N * K * 2) : (size_t)-1;
   return (size_t)-1;
 }
 
@@ -305,6 +306,47 @@ convrot_status convrot_linear_w8a8_ex(const void* X, int64_t M, int64_t K, const
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return linear_w8a8_impl(X, M, K, Q_W, s_W, N, bias, lora, residual, Y, workspace,
                           workspace_bytes, stream);
+}
+
+convrot_status convrot_dequantize_weights(const int8_t* Q_W, const float* s_W, int64_t N, int64_t K,
+                                          void* W16, void* stream) {
+  if (N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!Q_W || !s_W || !W16) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(Q_W) || !aligned16(s_W) || !aligned16(W16)) return CONVROT_ERR_ALIGNMENT;
+  const size_t wb = (size_t)N * K * 2;
+  if (overlap(W16, wb, Q_W, (size_t)N * K) || overlap(W16, wb, s_W, (size_t)N * 4))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  return launched(launch_dequantize(Q_W, s_W, N, K, W16, as_stream(stream)));
+}
+
+convrot_status convrot_linear_dequant(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
+                                      const float* s_W, int64_t N, const float* bias, void* Y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
+      (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
+    return CONVROT_ERR_ALIGNMENT;
+  const size_t need = convrot_workspace_bytes(CONVROT_PATH_DEQUANT, M, N, K, 0);
+  if (!workspace || workspace_bytes < need) return CONVROT_ERR_WORKSPACE;
+  const size_t yb = (size_t)M * N * 2, xb = (size_t)M * K * 2, qb = (size_t)N * K, sb = (size_t)N * 4;
+  const size_t bb = bias ? (size_t)N * 4 : 0;
+  if (overlap(Y, yb, X, xb) || overlap(Y, yb, Q_W, qb) || overlap(Y, yb, s_W, sb) ||
+      overlap(Y, yb, bias, bb) || overlap(Y, yb, workspace, need) || overlap(workspace, need, X, xb) ||
+      overlap(workspace, need, Q_W, qb) || overlap(workspace, need, s_W, sb) ||
+      overlap(workspace, need, bias, bb))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  hipStream_t s = as_stream(stream);
+  if (convrot_status st = launched(launch_dequantize(Q_W, s_W, N, K, workspace, s))) return st;
+  GemmArgs g{};
+  g.X = X; g.W = workspace; g.bias = bias; g.out = Y; g.M = M; g.N = N; g.K = K;
+  return launched(launch_gemm<GemmMode::kF16>(g, s));
 }
 
 convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const int8_t* Q_W,

@@ -217,6 +217,16 @@ gemm_dma_kernel(GemmArgs p) {
         swv[i][r] = p.sW[nc];
         bsv[i][r] = p.bias ? p.bias[nc] : 0.0f;
       }
+  } else if constexpr (MODE == GemmMode::kF16) {
+    if (p.bias) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t n = n0 + wn * WN + i * 16 + ocol + r;
+          bsv[i][r] = p.bias[n < N ? n : N - 1];
+        }
+    }
   }
 
   // LoRA operands of the first 32 rank columns (rows past M or N repeat the
@@ -509,7 +519,7 @@ gemm_dma_kernel(GemmArgs p) {
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(p.bias ? __fadd_rn(acc[i][j][r], bsv[i][r]) : acc[i][j][r]);
         }
         uint2 v;
         v.x = (uint32_t)__half_as_ushort(h[0]) | ((uint32_t)__half_as_ushort(h[1]) << 16);

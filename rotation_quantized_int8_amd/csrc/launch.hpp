@@ -12,7 +12,7 @@ struct GemmArgs {
   const void* W;        // [N, K] int8 (kI8*, kW8A16) or fp16 (kF16)
   const float* sX;      // [M]   (kI8toF16)
   const float* sW;      // [N]   (kI8toF16, kW8A16)
-  const float* bias;    // [N] or null
+  const float* bias;    // [N] or null (kI8toF16, kW8A16, kF16)
   const __half* R;      // [M, N] fp16 residual added to the fp16 output (kI8toF16), or null
   const __half* T;      // [M, t_ld] fp16 LoRA activation X down^T (kI8toF16, kW8A16)
   const __half* U;      // [N, t_ld] fp16 LoRA up weight U' = fp16(scale * up), zero past the rank
@@ -39,6 +39,9 @@ int64_t w8a8_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_splitk_epilogue(const int32_t* parts, int64_t splits, const GemmArgs& a,
                                   hipStream_t stream);
 
+// Dequantise-every-call baseline: W16 fp16 [N, K] = fp16((Q_W (.) s_W) H).
+hipError_t launch_dequantize(const int8_t* QW, const float* sW, int64_t N, int64_t K, void* W16,
+                             hipStream_t stream);
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* QW, float* sW,
                                    hipStream_t stream);
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,

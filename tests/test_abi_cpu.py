@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = cr.header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(L, name), name
     assert set(declared) == set(cr._SIGNATURES)
@@ -39,21 +39,26 @@ def test_workspace_bytes(L):
     assert L.convrot_workspace_bytes(0, 1024, 2048, 2048, 0) == 1024 * 2048 + 4096
     assert L.convrot_workspace_bytes(0, 3, 5, 256, 0) == 768 + 256
     assert L.convrot_workspace_bytes(1, 4, 8, 256, 0) == 2048
-    assert L.convrot_workspace_bytes(1, 4, 8, 256, 32) == 2048 + 256
+    # W8A16 with LoRA: X16, T fp16 [M, 32], U' fp16 [N, 32] (256-byte pieces)
+    assert L.convrot_workspace_bytes(1, 4, 8, 256, 32) == 2048 + 256 + 512
     assert L.convrot_workspace_bytes(0, 0, 5, 256, 0) == 0
     # few rows and a small tile grid: room for 8 K-split int32 partials
     assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 0) == 16 * 8192 + 256 + 8 * 16 * 2048 * 4
-    # a LoRA adds its fp16 low-rank activation [M, rank rounded up to 32] and,
-    # when K spans several 256-column chunks, fp32 partial sums per K range
-    assert L.convrot_workspace_bytes(0, 3, 5, 256, 17) == 768 + 256 + 256
+    # a LoRA adds its fp16 low-rank activation [M, t_ld], the fp16 scaled up
+    # weight [N, t_ld] (t_ld = rank rounded up to 32) and, when K spans
+    # several 256-column chunks, fp32 partial sums per K range
+    assert L.convrot_workspace_bytes(0, 3, 5, 256, 17) == 768 + 256 + 256 + 512
     assert L.convrot_workspace_bytes(0, 1024, 2048, 2048, 64) == \
-        1024 * 2048 + 4096 + 1024 * 64 * 2 + 8 * 1024 * 64 * 4
+        1024 * 2048 + 4096 + 1024 * 64 * 2 + 2048 * 64 * 2 + 8 * 1024 * 64 * 4
     bad = ctypes.c_size_t(-1).value
     assert L.convrot_workspace_bytes(0, 4, 4, 255, 0) == bad
     assert L.convrot_workspace_bytes(0, 4, 4, 131072 + 256, 0) == bad
     assert L.convrot_workspace_bytes(0, -1, 4, 256, 0) == bad
     assert L.convrot_workspace_bytes(1, 4, 4, 256, 65) == bad
     assert L.convrot_workspace_bytes(7, 4, 4, 256, 0) == bad
+    # dequantise-every-call: the fp16 weight [N, K]
+    assert L.convrot_workspace_bytes(2, 4, 8, 256, 0) == 8 * 256 * 2
+    assert L.convrot_workspace_bytes(2, 4, 8, 256, 4) == bad
 
 
 P = 1 << 20          # a fake, 16-byte aligned "device" address: never dereferenced
@@ -131,6 +136,24 @@ def test_linear_w8a16_argument_errors(L):
     assert f(P, 4, 256, Q, R, 8, None, ctypes.byref(lora), S, S + 4096, wsl, None) == ALIGN
     assert f(P, 4, 256, Q, R, 8, None, None, S, S + 4096, ws - 16, None) == WORKSPACE
     assert f(None, 0, 256, None, None, 8, None, None, None, None, 0, None) == OK
+
+
+def test_dequant_argument_errors(L):
+    f = L.convrot_linear_dequant
+    ws = L.convrot_workspace_bytes(2, 4, 8, 256, 0)
+    assert f(None, 0, 256, None, None, 8, None, None, None, 0, None) == OK
+    assert f(P, 4, 300, Q, R, 8, None, S, S + 8192, ws, None) == SHAPE
+    assert f(P, 4, 256, Q, R, 8, None, None, S + 8192, ws, None) == INVALID
+    assert f(P, 4, 256, Q, R, 8, R + 4096 + 8, S, S + 8192, ws, None) == ALIGN
+    assert f(P, 4, 256, Q, R, 8, None, S, S + 8192, ws - 1, None) == WORKSPACE
+    assert f(P, 4, 256, Q, R, 8, None, S, S, ws, None) == INVALID        # Y inside the workspace
+    assert f(P, 4, 256, Q, R, 8, None, S, Q, ws, None) == INVALID        # workspace over Q_W
+    d = L.convrot_dequantize_weights
+    assert d(None, None, 0, 256, None, None) == OK
+    assert d(P, Q, 8, 255, R, None) == SHAPE
+    assert d(P, Q, 8, 256, None, None) == INVALID
+    assert d(P, Q, 8, 256, P + 16, None) == INVALID
+    assert d(P, Q + 4, 8, 256, R, None) == ALIGN
 
 
 def test_stage_argument_errors(L):

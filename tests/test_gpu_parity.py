@@ -542,3 +542,47 @@ def test_gemm_f16_within_tolerance(M, N, K):
     bound = _ulp16(yo) + 2.0 ** -14 * s
     d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
     assert int((d > bound).sum()) == 0
+
+
+# --------------------------------- dequantise-every-call baseline (next-4)
+
+@pytest.mark.parametrize("N,K", [(256, 256), (80, 512), (37, 768), (3, 8192)])
+def test_dequantize_weights_bitexact(N, K):
+    _say(f"dequantize weights N={N} K={K}")
+    qw, sw = O.quantize_weights(wl.make_weights(N, K, seed=N + K).numpy())
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    wg = _np(cr.dequantize_weights(t(qw), t(sw)))
+    wo = O.dequantize_weights(qw, sw)
+    assert np.array_equal(wg.view(np.uint16), wo.view(np.uint16))
+
+
+@pytest.mark.parametrize("N,K", [(n, k) for (n, k, _) in wl.LAYER_SHAPES])
+def test_dequantize_weights_bitexact_full_shapes(N, K):
+    # every element on the GPU; the oracle on 64 sampled rows plus the first and last
+    _say(f"dequantize weights full N={N} K={K}")
+    qw, sw = O.quantize_weights(wl.make_weights(N, K, seed=1).numpy())
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    wg = _np(cr.dequantize_weights(t(qw), t(sw)))
+    rows = np.unique(np.concatenate([np.random.default_rng(N).choice(N, min(N, 64), replace=False), [0, N - 1]]))
+    wo = O.dequantize_weights(qw[rows], sw[rows])
+    assert np.array_equal(wg[rows].view(np.uint16), wo.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K,bias", [(64, 256, 256, False), (300, 203, 768, True), (1024, 2048, 2048, True),
+                                        (5, 200, 4096, False)])
+def test_linear_dequant_within_tolerance(M, N, K, bias):
+    _say(f"linear dequant M={M} N={N} K={K} bias={bias}")
+    x = wl.make_activations(M, K, seed=M + 5)
+    qw, sw = O.quantize_weights(wl.make_weights(N, K, seed=M + 5).numpy())
+    b = wl.make_bias(N, seed=M + 5) if bias else None
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    yg = _np(cr.linear_dequant(x.to(DEV), t(qw), t(sw), None if b is None else b.to(DEV)))
+    yo = O.linear_dequant(x.numpy(), qw, sw, None if b is None else b.numpy())
+    wd = O.dequantize_weights(qw, sw).astype(np.float64)
+    s_main = np.abs(x.numpy().astype(np.float64)) @ np.abs(wd).T
+    bound = _ulp16(yo) + 2.0 ** -14 * s_main
+    d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
+    viol = int((d > bound).sum())
+    rel = float(np.linalg.norm(d) / np.linalg.norm(yo.astype(np.float64)))
+    _say(f"  violations {viol}, max |dY|/bound {float((d / bound).max()):.3f}, rel. Frobenius {rel:.2e}")
+    assert viol == 0 and rel <= 1e-3
