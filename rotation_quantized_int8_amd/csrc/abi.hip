@@ -104,9 +104,9 @@ size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_
   if (M == 0 || N == 0) return 0;
   if (!k_ok(K)) return (size_t)-1;
   if (path == CONVROT_PATH_W8A8) {
-    const int64_t splits = w8a8_splits(M, N, K);
+    const W8A8Plan plan = w8a8_plan(M, N, K, lora_rank > 0);
     return round256((size_t)M * K) + round256((size_t)M * 4) +
-           (splits > 1 ? round256((size_t)splits * M * N * 4) : 0) + lora_ws_bytes(M, N, K, lora_rank);
+           (plan.parts ? round256((size_t)plan.splits * M * N * 4) : 0) + lora_ws_bytes(M, N, K, lora_rank);
   }
   if (path == CONVROT_PATH_W8A16) return round256((size_t)M * K * 2) + lora_ws_bytes(M, N, K, lora_rank);
   if (path == CONVROT_PATH_DEQUANT) return lora_rank == 0 ? round256((size_t)N * K * 2) : (size_t)-1;
@@ -258,17 +258,25 @@ convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_
     return CONVROT_ERR_INVALID_ARG;
   if (convrot_status st = check_device()) return st;
   hipStream_t s = as_stream(stream);
-  const int64_t splits = w8a8_splits(M, N, K);
+  const W8A8Plan plan = w8a8_plan(M, N, K, lora != nullptr);
+  const int64_t splits = plan.splits;
   char* ws = reinterpret_cast<char*>(workspace);
   int8_t* QX = reinterpret_cast<int8_t*>(ws);
   size_t off = round256((size_t)M * K);
   float* sX = reinterpret_cast<float*>(ws + off);
   off += round256((size_t)M * 4);
   int32_t* parts = reinterpret_cast<int32_t*>(ws + off);
-  if (splits > 1) off += round256((size_t)splits * M * N * 4);
+  if (plan.parts) off += round256((size_t)splits * M * N * 4);
   const LoraWs lw = lora_ws(ws + off, M, N, K, rank);
   const int t_ld = lora_ld(rank);
 
+  if (plan.kind == W8A8Plan::kFused) {   // one launch: quantisation, product and epilogue
+    GemmArgs g{};
+    g.W = Q_W; g.sW = s_W; g.bias = bias; g.out = Y;
+    g.R = reinterpret_cast<const __half*>(residual);
+    g.M = M; g.N = N; g.K = K;
+    return launched(launch_skinny_fused(g, X, s));
+  }
   if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s))) return st;
   if (lora) {
     if (convrot_status st = launched(launch_lora_prep(X, lora->down, lora->up, lora->scale, M, N, K,
@@ -280,7 +288,12 @@ convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_
   g.R = reinterpret_cast<const __half*>(residual);
   g.T = lw.T; g.U = lw.U; g.t_ld = t_ld;
   g.M = M; g.N = N; g.K = K;
-  if (splits > 1) {   // few rows: int32 partials over K splits, then the epilogue
+  if (plan.kind == W8A8Plan::kSkinny) {
+    if (!plan.parts) return launched(launch_skinny(g, 1, nullptr, s));
+    if (convrot_status st = launched(launch_skinny(g, splits, parts, s))) return st;
+    return launched(launch_splitk_epilogue(parts, splits, g, s));
+  }
+  if (plan.parts) {   // few rows: int32 partials over K splits, then the epilogue
     GemmArgs gi{};
     gi.X = QX; gi.W = Q_W; gi.out = parts; gi.M = M; gi.N = N; gi.K = K; gi.kc = K / splits;
     if (convrot_status st = launched(launch_gemm<GemmMode::kI8toI32>(gi, s))) return st;

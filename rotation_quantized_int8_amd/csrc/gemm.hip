@@ -12,81 +12,124 @@ namespace convrot {
 // 128x64 tiles spread the work wider, and when even those would leave half
 // the CUs idle, 64x64 or 32x64 tiles do.  The 256x128 tile runs as 8 waves
 // of 64x64 (two per SIMD, so one wave's waits overlap the other's MFMAs).
-// With few rows (M <= 128) the product streams the weights, and 32x64 tiles
-// keep the activation loads from being mostly padding while giving four
-// times as many workgroups.
+// With few rows (M <= 128) the int8 product streams the weights: the widest
+// of 64x64, 32x64 and 16x64 (256-byte K slices, 6 stages) tiles that still
+// gives at least 192 workgroups, else 16x64; the other products use 32x64.
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
-  (void)mode; (void)K;
-  if (M <= 128) return 9;
+  (void)K;
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (M <= 128) {
+    if (mode != GemmMode::kI8toF16 && mode != GemmMode::kI8toI32) return 9;
+    if (tiles(64, 64) >= 192) return 10;
+    if (tiles(32, 64) >= 192) return 9;
+    return 15;
+  }
   if (tiles(256, 128) >= 160) return 13;
   if (tiles(128, 64) >= 128) return 8;
   if (tiles(64, 64) >= 128) return 10;
   return 9;
 }
 
-// W8A8 with few rows: when the 32x64 tile grid is too small to occupy the
-// chip (fewer than 64 tiles), K is split so that tiles x splits reaches about
-// 256 workgroups with at least 512 K values each.  The int32 partial sums are
+// W8A8 through the tiled GEMM with few rows: when even the chosen tiles
+// give fewer than 32 workgroups, K is split so that tiles x splits reaches
+// about 128 with at least 2048 K values each.  The int32 partial sums are
 // exact, so the split result is bit-identical to the unsplit one.
 int64_t w8a8_splits(int64_t M, int64_t N, int64_t K) {
   if (M > 128) return 1;
-  const int64_t tiles = ((M + 31) / 32) * ((N + 63) / 64);
-  if (tiles >= 64) return 1;
+  const int cfg = choose_gemm_cfg(GemmMode::kI8toI32, M, N, K);
+  const int64_t bm = cfg == 10 ? 64 : cfg == 9 ? 32 : 16;
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + 63) / 64);
+  if (tiles >= 32) return 1;
   int64_t s = 1;
-  while (tiles * s * 2 <= 256 && K % (s * 2 * 256) == 0 && K / (s * 2) >= 512) s *= 2;
+  while (tiles * s * 2 <= 128 && K % (s * 2 * 256) == 0 && K / (s * 2) >= 2048) s *= 2;
   return s;
+}
+
+// Few rows: one fused launch when every workgroup can quantise the rows
+// itself; up to 16 rows and at most 4096 outputs per row, the few-row kernel
+// (16-row weight blocks leave the tiled GEMM too few workgroups there);
+// otherwise the tiled GEMM.
+W8A8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, bool lora) {
+  if (!lora && skinny_fusable(M, K)) return {W8A8Plan::kFused, 1, false};
+  if (M <= 16 && N <= 4096) {
+    const int64_t s = skinny_splits(N, K);
+    return {W8A8Plan::kSkinny, s, lora || s > 1};
+  }
+  const int64_t s = w8a8_splits(M, N, K);
+  return {W8A8Plan::kGemm, s, s > 1};
 }
 
 namespace {
 
-constexpr int kEpiRows = 4;   // rows per thread of the split-K epilogue
+constexpr int kSplitBatch = 8;   // K-range partials loaded together
 
-// One thread per output column n and kEpiRows rows (the loads of all its
-// rows go out together, and the column's s_W, bias and LoRA up values are
-// fetched once for them):
+// One thread per output row m and 4 consecutive columns n .. n + 3 (one
+// 16-byte piece of every K range's int32 partial; all ranges' pieces are in
+// flight together, kSplitBatch at a time):
 //   y = fp32(sum_z A_z) * fp32(s_X * s_W) [+ bias]   (the GEMM epilogue's
 //       fp32 operations in the same order),
 //   [+ LoRA term sum_r T[m, r] U'[n, r] accumulated in fp32],
 //   Y = fp16(y) [then one fp16 addition of the residual].
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 splitk_epilogue_kernel(const int32_t* __restrict__ parts, int64_t splits, GemmArgs p) {
-  const int64_t n = (int64_t)blockIdx.x * 64 + threadIdx.x;
   const int64_t M = p.M, N = p.N, total = M * N;
-  if (n >= N) return;
-  const int64_t m0 = (int64_t)blockIdx.y * kEpiRows;
-  int32_t a[kEpiRows];
-  float l[kEpiRows];
+  const int64_t q = (N + 3) / 4;                  // pieces per row
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= M * q) return;
+  const int64_t m = e / q;
+  const int64_t n0 = 4 * (e - m * q);
+  const int cols = N - n0 < 4 ? (int)(N - n0) : 4;
+  const bool vec = (N % 4) == 0;                  // 16-byte aligned pieces
+  const int32_t* base = parts + m * N + n0;
+
+  int32_t a[4] = {0, 0, 0, 0};
+  for (int64_t z0 = 0; z0 < splits; z0 += kSplitBatch) {
+    v4i v[kSplitBatch];
 #pragma unroll
-  for (int i = 0; i < kEpiRows; ++i) {
-    a[i] = 0;
-    l[i] = 0.0f;
-  }
-  for (int64_t z = 0; z < splits; ++z) {
+    for (int u = 0; u < kSplitBatch; ++u) {
+      v[u] = v4i{0, 0, 0, 0};
+      if (z0 + u < splits) {
+        const int32_t* src = base + (z0 + u) * total;
+        if (vec) {
+          v[u] = *reinterpret_cast<const v4i*>(src);
+        } else {
+          for (int c = 0; c < cols; ++c) v[u][c] = src[c];
+        }
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < kEpiRows; ++i)
-      if (m0 + i < M) a[i] += parts[z * total + (m0 + i) * N + n];
+    for (int u = 0; u < kSplitBatch; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] += v[u][c];
   }
+
+  float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int r = 0; r < p.t_ld; ++r) {
-    const float u = __half2float(p.U[n * p.t_ld + r]);
+    const float t = __half2float(p.T[m * p.t_ld + r]);
 #pragma unroll
-    for (int i = 0; i < kEpiRows; ++i)
-      if (m0 + i < M) l[i] = fmaf(__half2float(p.T[(m0 + i) * p.t_ld + r]), u, l[i]);
+    for (int c = 0; c < 4; ++c)
+      if (c < cols) l[c] = fmaf(t, __half2float(p.U[(n0 + c) * p.t_ld + r]), l[c]);
   }
   __half* Y = reinterpret_cast<__half*>(p.out);
-  const float sw = p.sW[n];
-  const float b = p.bias ? p.bias[n] : 0.0f;
+  const float sx = p.sX[m];
+  __half h[4];
 #pragma unroll
-  for (int i = 0; i < kEpiRows; ++i) {
-    const int64_t m = m0 + i;
-    if (m >= M) break;
-    const int64_t e = m * N + n;
-    float y = __fmul_rn((float)a[i], __fmul_rn(p.sX[m], sw));
-    if (p.bias) y = __fadd_rn(y, b);
-    if (p.t_ld > 0) y = __fadd_rn(y, l[i]);
-    __half h = __float2half_rn(y);
-    if (p.R) h = __float2half_rn(__half2float(h) + __half2float(p.R[e]));
-    Y[e] = h;
+  for (int c = 0; c < 4; ++c) {
+    if (c >= cols) break;
+    const int64_t n = n0 + c;
+    float y = __fmul_rn((float)a[c], __fmul_rn(sx, p.sW[n]));
+    if (p.bias) y = __fadd_rn(y, p.bias[n]);
+    if (p.t_ld > 0) y = __fadd_rn(y, l[c]);
+    h[c] = __float2half_rn(y);
+    if (p.R) h[c] = __float2half_rn(__half2float(h[c]) + __half2float(p.R[m * N + n]));
+  }
+  if (vec) {
+    uint2 o;
+    o.x = (uint32_t)__half_as_ushort(h[0]) | ((uint32_t)__half_as_ushort(h[1]) << 16);
+    o.y = (uint32_t)__half_as_ushort(h[2]) | ((uint32_t)__half_as_ushort(h[3]) << 16);
+    *reinterpret_cast<uint2*>(Y + m * N + n0) = o;
+  } else {
+    for (int c = 0; c < cols; ++c) Y[m * N + n0 + c] = h[c];
   }
 }
 
@@ -94,8 +137,9 @@ splitk_epilogue_kernel(const int32_t* __restrict__ parts, int64_t splits, GemmAr
 
 hipError_t launch_splitk_epilogue(const int32_t* parts, int64_t splits, const GemmArgs& a,
                                   hipStream_t stream) {
-  const dim3 grid((unsigned)((a.N + 63) / 64), (unsigned)((a.M + kEpiRows - 1) / kEpiRows));
-  hipLaunchKernelGGL(splitk_epilogue_kernel, grid, dim3(64), 0, stream, parts, splits, a);
+  const int64_t threads = a.M * ((a.N + 3) / 4);
+  hipLaunchKernelGGL(splitk_epilogue_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     parts, splits, a);
   return hipGetLastError();
 }
 

@@ -573,6 +573,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const size_t lds = (size_t)ST * ((size_t)BM * XS + (size_t)BN * kRowW);
   auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST, XS, EXTRA>;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;   // more than one CU's LDS
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -599,6 +600,7 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
         case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4, true>(a, stream);
         case 10: return launch_cfg<MODE, 2, 2, 2, 2, 4, true>(a, stream);
         case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3, true>(a, stream);
+        case 15: return launch_cfg<MODE, 1, 4, 1, 1, 6, true, 256>(a, stream);
         default: return hipErrorInvalidValue;
       }
     }
@@ -619,6 +621,10 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 12: return launch_cfg<MODE, 1, 4, 2, 4, 3>(a, stream);  // 32x256
     case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3>(a, stream);  // 256x128, 8 waves
     case 14: return launch_cfg<MODE, 2, 4, 4, 4, 3>(a, stream);  // 128x256, 8 waves
+    case 15: return launch_cfg<MODE, 1, 4, 1, 1, 6, false, 256>(a, stream);  // 16x64, 256-byte K slices
+    case 16: return launch_cfg<MODE, 1, 4, 1, 1, 7, false, 256>(a, stream);  // 16x64, 7 stages
+    case 17: return launch_cfg<MODE, 1, 4, 1, 2, 4, false, 256>(a, stream);  // 16x128
+    case 18: return launch_cfg<MODE, 2, 2, 1, 2, 6, false, 256>(a, stream);  // 32x64, 256-byte K slices
     default: return hipErrorInvalidValue;
   }
 }

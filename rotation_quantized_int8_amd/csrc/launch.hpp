@@ -31,8 +31,29 @@ template <GemmMode MODE>
 hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream);
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K);
 
-// Split-K plan of the W8A8 linear: number of K splits (1 = none) for a size.
+// Few-row W8A8 product (M <= 32): K ranges for a size, and the launch
+// (parts == nullptr: one range and the scale epilogue [+ bias, residual] in
+// the kernel; else int32 partials [splits, M, N] for launch_splitk_epilogue).
+int64_t skinny_splits(int64_t N, int64_t K);
+hipError_t launch_skinny(const GemmArgs& a, int64_t splits, int32_t* parts, hipStream_t stream);
+// The whole W8A8 layer in one launch for M K <= 8192 (every workgroup
+// quantises the activations X fp16 [M, K] itself); a.X is unused.
+bool skinny_fusable(int64_t M, int64_t K);
+hipError_t launch_skinny_fused(const GemmArgs& a, const void* X, hipStream_t stream);
+
+// Split-K plan of the W8A8 GEMM path (M > 32): number of K splits (1 = none).
 int64_t w8a8_splits(int64_t M, int64_t N, int64_t K);
+
+// How the W8A8 linear runs for a size: one fused launch (few rows, short
+// rows, no LoRA), the prologue and the few-row kernel (M <= 32), or the
+// prologue and the tiled GEMM; `parts` says whether int32 partials
+// [splits, M, N] go through the workspace to the K-split epilogue.
+struct W8A8Plan {
+  enum Kind { kFused, kSkinny, kGemm } kind;
+  int64_t splits;
+  bool parts;
+};
+W8A8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, bool lora);
 // Y = fp16(fp32(sum_z A_z) * fp32(s_X s_W) [+ bias]) from the int32 partials,
 // then the optional LoRA term (a.T, a.U, a.t_ld) before the fp16 rounding and
 // the optional residual a.R after it.

@@ -42,12 +42,18 @@ def test_workspace_bytes(L):
     # W8A16 with LoRA: X16, T fp16 [M, 32], U' fp16 [N, 32] (256-byte pieces)
     assert L.convrot_workspace_bytes(1, 4, 8, 256, 32) == 2048 + 256 + 512
     assert L.convrot_workspace_bytes(0, 0, 5, 256, 0) == 0
-    # few rows and a small tile grid: room for 8 K-split int32 partials
-    assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 0) == 16 * 8192 + 256 + 8 * 16 * 2048 * 4
+    # few rows: the few-row kernel covers 2048 outputs without splitting K ...
+    assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 0) == 16 * 8192 + 256
+    # ... but 256 outputs get 4 K ranges of int32 partials
+    assert L.convrot_workspace_bytes(0, 16, 256, 8192, 0) == 16 * 8192 + 256 + 4 * 16 * 256 * 4
+    # with a LoRA the few-row product always goes through int32 partials
+    assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 32) == \
+        16 * 8192 + 256 + 16 * 2048 * 4 + 16 * 32 * 2 + 2048 * 32 * 2 + 32 * 16 * 32 * 4
     # a LoRA adds its fp16 low-rank activation [M, t_ld], the fp16 scaled up
     # weight [N, t_ld] (t_ld = rank rounded up to 32) and, when K spans
     # several 256-column chunks, fp32 partial sums per K range
-    assert L.convrot_workspace_bytes(0, 3, 5, 256, 17) == 768 + 256 + 256 + 512
+    # (M = 3 with a LoRA: also the int32 product of the few-row kernel)
+    assert L.convrot_workspace_bytes(0, 3, 5, 256, 17) == 768 + 256 + 256 + 256 + 512
     assert L.convrot_workspace_bytes(0, 1024, 2048, 2048, 64) == \
         1024 * 2048 + 4096 + 1024 * 64 * 2 + 2048 * 64 * 2 + 8 * 1024 * 64 * 4
     bad = ctypes.c_size_t(-1).value

@@ -586,3 +586,34 @@ def test_linear_dequant_within_tolerance(M, N, K, bias):
     rel = float(np.linalg.norm(d) / np.linalg.norm(yo.astype(np.float64)))
     _say(f"  violations {viol}, max |dY|/bound {float((d / bound).max()):.3f}, rel. Frobenius {rel:.2e}")
     assert viol == 0 and rel <= 1e-3
+
+
+# ------------------------------------------ few activation rows (next-1)
+# M <= 16 with M K <= 8192 runs as one fused launch; M <= 16 with N <= 4096
+# otherwise runs the prologue and the few-row kernel (K split into int32
+# partials when N is small); larger M the tiled GEMM with narrow tiles (K
+# split when even those give few workgroups).  All bit-exact.
+
+@pytest.mark.parametrize("M,N,K,bias", [(1, 8192, 2048, False), (1, 2048, 8192, True), (4, 2048, 2048, True),
+                                        (16, 6144, 256, False), (3, 203, 768, True), (2, 8, 4096, False),
+                                        (16, 2048, 8192, True), (32, 8192, 2048, False), (17, 300, 4096, True),
+                                        (8, 256, 8192, False), (24, 1000, 1024, True), (1, 256, 131072, False),
+                                        (24, 64, 65536, True), (100, 128, 16384, False), (128, 8192, 2048, True),
+                                        (64, 6144, 256, False)])
+def test_linear_w8a8_few_rows_bitexact(M, N, K, bias):
+    _say(f"linear w8a8 few rows M={M} N={N} K={K} bias={bias}")
+    mism, emax, rel = _w8a8_case(M, N, K, seed=3 * M + K, bias=bias)
+    assert mism == 0 and emax == 0.0
+
+
+@pytest.mark.parametrize("M,N,K,rank", [(1, 2048, 2048, 0), (4, 8192, 2048, 0), (16, 2048, 8192, 0),
+                                        (8, 256, 8192, 0), (1, 2048, 2048, 32), (16, 2048, 8192, 32),
+                                        (24, 64, 16384, 0), (24, 64, 16384, 32), (32, 8192, 2048, 32)])
+def test_linear_w8a8_ex_few_rows(M, N, K, rank):
+    _say(f"linear w8a8_ex few rows M={M} N={N} K={K} rank={rank}")
+    yg, yo, tol = _w8a8_ex_case(M, N, K, seed=M + K + rank, bias=True, rank=rank, in_place=(M == 4))
+    if rank == 0:
+        assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+    else:
+        d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
+        assert int((d > tol).sum()) == 0
