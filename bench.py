@@ -174,43 +174,60 @@ M_SWEEP_SHAPES = ((8192, 2048), (2048, 8192))
 
 def m_sweep(cr, L, stream, dev):
     """W8A8 end to end and fp16 F.linear at several row counts on the two large
-    shapes (hot buffers; median of 5 sets of 10 calls, graph-captured)."""
+    shapes, graph-captured: hot (the same weights every call, median of 5 sets
+    of 10 calls, the pages' protocol) and cold (every call its own weight copy,
+    the copies together larger than the 256 MB memory-side cache, mean over 3
+    replays)."""
     import torch
     import torch.nn.functional as F
     import workload as wl
     rows = []
+    cold_bytes = 384 << 20
     for (N, K) in M_SWEEP_SHAPES:
         w = wl.make_weights(N, K, seed=0).to(dev)
         qw, sw = cr.quantize_weights(w)
         w16 = w.to(torch.float16)
         del w
+        qcold = [qw.clone() for _ in range(max(2, cold_bytes // (N * K)))]
+        wcold = [w16.clone() for _ in range(max(2, cold_bytes // (2 * N * K)))]
         for M in M_SWEEP:
             x = wl.make_activations(M, K, seed=0).to(dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             ws = torch.empty(cr.workspace_bytes(cr.PATH_W8A8, M, N, K), dtype=torch.uint8, device=dev)
 
-            def w8a8():
-                h = torch.cuda.current_stream().cuda_stream
-                for _ in range(10):
-                    st = L.convrot_linear_w8a8(x.data_ptr(), M, K, qw.data_ptr(), sw.data_ptr(), N, None,
-                                               y.data_ptr(), ws.data_ptr(), ws.numel(), h)
-                    if st:
-                        raise RuntimeError(L.convrot_status_string(st).decode())
+            def w8a8_calls(weights):
+                def run():
+                    h = torch.cuda.current_stream().cuda_stream
+                    for q in weights:
+                        st = L.convrot_linear_w8a8(x.data_ptr(), M, K, q.data_ptr(), sw.data_ptr(), N, None,
+                                                   y.data_ptr(), ws.data_ptr(), ws.numel(), h)
+                        if st:
+                            raise RuntimeError(L.convrot_status_string(st).decode())
+                return run
 
-            def f16():
-                for _ in range(10):
-                    F.linear(x, w16)
+            def f16_calls(weights):
+                def run():
+                    for w_ in weights:
+                        F.linear(x, w_)
+                return run
 
             row = {"N": N, "K": K, "M": M}
-            for name, fn in (("w8a8_us", w8a8), ("fp16_torch_linear_us", f16)):
+            for name, fn, calls in (("w8a8_us", w8a8_calls([qw] * 10), 10),
+                                    ("fp16_torch_linear_us", f16_calls([w16] * 10), 10)):
                 g = capture(fn, stream)
-                row[name] = round(median_sets(g, 5, stream) / 10 * 1e3, 3)
+                row[name] = round(median_sets(g, 5, stream) / calls * 1e3, 3)
+                del g
+            for name, fn, calls in (("w8a8_cold_us", w8a8_calls(qcold), len(qcold)),
+                                    ("fp16_torch_linear_cold_us", f16_calls(wcold), len(wcold))):
+                g = capture(fn, stream)
+                row[name] = round(timed_graph(g, 3, 1, stream) / calls * 1e3, 3)
                 del g
             row["w8a8_tops"] = round(2.0 * M * N * K / (row["w8a8_us"] * 1e-6) / 1e12, 1)
             row["w8a8_weight_gbs"] = round(N * K / (row["w8a8_us"] * 1e-6) / 1e9, 1)
+            row["w8a8_cold_weight_gbs"] = round(N * K / (row["w8a8_cold_us"] * 1e-6) / 1e9, 1)
             rows.append(row)
             del x, y, ws
-        del qw, sw, w16
+        del qw, sw, w16, qcold, wcold
     return rows
 
 
