@@ -48,7 +48,16 @@ Readings where the pages leave a step open:
   R10 the dequantise-every-call baseline ([P1] "What changed in the
       computation": the earlier patch turned Q_W (.) s_W back into fp16,
       un-rotated it and ran the plain X W^T): W_deq = fp16(exact (Q_W (.) s_W) H),
-      one rounding (H is its own inverse), then Y = fp16(exact X W_deq^T + bias).
+      one rounding (H is its own inverse), then Y = fp16(exact X W_deq^T + bias);
+  R11 the range-safe weight-only path ([P4] "Design", range safety by
+      construction): each activation row (fp16 or bf16) is rotated exactly and
+      divided by 2^e_m, e_m the smallest integer with max|X_rot[m,:]| <= 2^e_m
+      (0 for a zero row), before the one rounding to fp16; the epilogue
+      multiplies by 2^e_m again, so Y = out(exact 2^e_m s_W[n] sum_k X16s Q_W
+      + bias) with one rounding to the output type (fp16 or bf16), and a
+      residual is one addition in that type.  The fp32 accumulation of the
+      MFMA path has no K limit (the pages' fp16 accumulation needs fp32 for
+      K > 65504).
 """
 
 from __future__ import annotations
@@ -67,6 +76,7 @@ QMAX = 127.0
 
 F32 = (24, -126, 127)     # (significand bits p, emin, emax)
 F16 = (11, -14, 15)
+BF16 = (8, -126, 127)
 
 
 def round_scaled_int(t: int, shift: int, fmt=F32) -> float:
@@ -375,6 +385,108 @@ def linear_dequant(x16, qw, sw, bias=None) -> np.ndarray:
     if bias is not None:
         y = y + np.asarray(bias, np.float32).astype(np.float64)[None, :]
     return y.astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# range-safe weight-only path  ([P4] "Design", reading R11)
+# ---------------------------------------------------------------------------
+
+def to_bf16(a) -> np.ndarray:
+    """Round float64 values to bfloat16 (round half to even), returned as float32.
+
+    Normal range: keep 8 significand bits of the float64 value; below 2^-126
+    the grid is 2^-133; at or beyond the overflow boundary (2 - 2^-8) 2^127
+    the result is +-inf, as IEEE round-to-nearest gives.
+    """
+    a = np.asarray(a, np.float64)
+    out = np.empty(a.shape, np.float64)
+    flat, res = a.ravel(), out.reshape(-1)
+    for i, v in enumerate(flat):
+        if v == 0 or not math.isfinite(v):
+            res[i] = v
+            continue
+        f, e = math.frexp(abs(v))                 # |v| = f 2^e, f in [0.5, 1)
+        q = max(e - 8, -133)                      # exponent of one unit in the last place
+        m = abs(v) / 2.0 ** q                     # exact (power-of-two scaling)
+        r = np.round(m)                           # half to even
+        val = math.copysign(r * 2.0 ** q, v)
+        res[i] = val if abs(val) < 2.0 ** 128 else math.copysign(math.inf, v)
+    return out.astype(np.float32)
+
+
+def _row_rotation_exact(x32_row) -> list:
+    """Exact X_rot values of one row (fp32-representable inputs) as Fractions."""
+    t = exact_int_of_f32(np.asarray(x32_row, np.float32).reshape(-1, GROUP))
+    t = t.dot(hadamard256_pm1().astype(object)).reshape(-1)
+    from fractions import Fraction
+    return [Fraction(int(v), 1 << (149 + 4)) for v in t]
+
+
+def rotate_rowscaled_f16(x):
+    """Range-safe prologue (reading R11): (X16s fp16 [M, K], e int64 [M]).
+
+    X16s = fp16(X_rot 2^-e_m) rounded once from the exact rotation, e_m the
+    smallest integer with max|X_rot[m, :]| <= 2^e_m (0 for a zero row).  The
+    input holds fp16 or bf16 values (any fp32 values work).  Rows whose
+    float64 rotation is exact (every group spanning at most 45 binades, which
+    keeps each partial sum within 53 bits) take the float64 route; others are
+    rotated with Python integers.
+    """
+    x = np.asarray(x, np.float32)
+    M, K = x.shape
+    _check_k(K)
+    xr = rotate_f64(x.astype(np.float64))
+    g = x.reshape(M, K // GROUP, GROUP).astype(np.float64)
+    nz = g != 0
+    _, ex = np.frexp(g)
+    lo = np.where(nz, np.maximum(ex - 24, -149), 10_000).min(axis=2)
+    hi = np.where(nz, ex, -10_000).max(axis=2)
+    exact_row = ~(((hi + 8 - lo) > 52) & nz.any(axis=2)).any(axis=1)
+    x16 = np.empty((M, K), np.float16)
+    e = np.zeros(M, np.int64)
+    for m in range(M):
+        if exact_row[m]:
+            amax = float(np.max(np.abs(xr[m])))
+            if amax > 0:
+                f, ex2 = math.frexp(amax)
+                e[m] = ex2 - 1 if f == 0.5 else ex2
+            x16[m] = (xr[m] * 2.0 ** -int(e[m])).astype(np.float16)
+        else:
+            vals = _row_rotation_exact(x[m])
+            amax = max(abs(v) for v in vals)
+            em = 0
+            if amax > 0:
+                em = math.ceil(math.log2(amax))
+                while amax > 2 ** em:                   # guard the float log
+                    em += 1
+                while em > -10_000 and amax <= 2 ** (em - 1):
+                    em -= 1
+            e[m] = em
+            for k, v in enumerate(vals):
+                sv = v / (2 ** em) if em >= 0 else v * (2 ** -em)
+                sh = sv.denominator.bit_length() - 1
+                x16[m, k] = round_scaled_int(sv.numerator, sh, F16)
+    return x16, e
+
+
+def linear_w8a16_rs(x, qw, sw, bias=None, residual=None, out="f16") -> np.ndarray:
+    """Range-safe weight-only linear (reading R11), output fp16 or bf16 (as float32).
+
+    The product of the scaled fp16 activations and the int8 codes is exact in
+    float64 (multiples of 2^-24 below 2^24); the scale, the exponent restore
+    and the bias are applied in float64 and rounded once to the output type;
+    a residual (same type) is then one addition rounded once.
+    """
+    x16s, e = rotate_rowscaled_f16(x)
+    acc = x16s.astype(np.float64) @ np.asarray(qw, np.int8).astype(np.float64).T
+    y = acc * np.asarray(sw, np.float32).astype(np.float64)[None, :] * np.exp2(e.astype(np.float64))[:, None]
+    if bias is not None:
+        y = y + np.asarray(bias, np.float32).astype(np.float64)[None, :]
+    rnd = (lambda a: np.asarray(a, np.float64).astype(np.float16)) if out == "f16" else to_bf16
+    y = rnd(y)
+    if residual is not None:
+        y = rnd(np.asarray(y, np.float64) + np.asarray(residual, np.float32).astype(np.float64))
+    return y
 
 
 def linear_f16(x16, w16) -> np.ndarray:

@@ -580,3 +580,88 @@ def test_linear_dequant_is_fp16_matmul_of_the_dequantised_weight():
         for n in range(6):
             exact = sum(Fraction(float(x16[m, k])) * Fraction(float(wd[n, k])) for k in range(256)) + Fraction(float(b[n]))
             assert float(y[m, n]) == _rt16(exact)
+
+
+# ---------------------------------------- range-safe weight-only path (R11)
+
+def test_to_bf16_matches_torch_cast():
+    import torch
+    rng = np.random.default_rng(40)
+    v = np.concatenate([rng.normal(0, 1, 2000) * 10.0 ** rng.integers(-40, 38, 2000),
+                        [3.39e38, 3.4e38, -3.4e38, 1e-40, 2.0 ** -133, 2.0 ** -134, 1.5 * 2.0 ** -134,
+                         1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 0.0]]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+    got = O.to_bf16(v.astype(np.float64))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_rowscaled_near_max_fp16_row_stays_finite():
+    # a constant row c rotates to 16 c in the first element of each group:
+    # 16 * 65504 = 2^20 (1 - 2^-11) overflows fp16, the scaled value is the
+    # largest fp16 below 1 with e = 20
+    x = np.full((1, 512), 65504.0, np.float32)
+    assert np.isinf(O.rotate_activations_f16(x.astype(np.float16))).any()
+    x16, e = O.rotate_rowscaled_f16(x)
+    assert e[0] == 20
+    assert float(x16[0, 0]) == 1 - 2.0 ** -11 and float(x16[0, 256]) == 1 - 2.0 ** -11
+    assert np.count_nonzero(x16) == 2
+
+
+def test_rowscaled_power_of_two_max_and_zero_row():
+    x = np.zeros((2, 256), np.float32)
+    x[0, 0] = 16 * 2.0 ** 5            # rotates to 2^5 at every position of the group
+    x16, e = O.rotate_rowscaled_f16(x)
+    assert e.tolist() == [5, 0]
+    assert np.all(x16[0] == 1.0) and np.all(x16[1] == 0)
+
+
+def test_rowscaled_equals_unscaled_fp16_in_normal_range():
+    rng = np.random.default_rng(41)
+    x = rng.integers(-8, 9, (6, 768)).astype(np.float16)
+    x16, e = O.rotate_rowscaled_f16(x.astype(np.float32))
+    ref = O.rotate_activations_f16(x)
+    restored = x16.astype(np.float64) * np.exp2(e.astype(np.float64))[:, None]
+    assert np.array_equal(restored, ref.astype(np.float64))
+    assert np.all(np.abs(x16).max(axis=1) <= 1) and np.all(np.abs(x16).max(axis=1) > 0.5)
+
+
+def test_rowscaled_bf16_huge_and_integer_path():
+    # bf16-sized values far beyond fp16 range; the Python-integer route for a
+    # row whose groups span more than 45 binades agrees with exact rationals
+    rng = np.random.default_rng(42)
+    x = O.to_bf16(rng.normal(0, 1, (3, 256)) * 1e30)
+    x[2, :4] = O.to_bf16([1e30, 1e-30, -3e20, 7e-25])     # wide span: integer route
+    x16, e = O.rotate_rowscaled_f16(x)
+    assert np.isfinite(x16.astype(np.float64)).all()
+    for m in range(3):
+        vals = O._row_rotation_exact(x[m])
+        for k in (0, 1, 100, 255):
+            sv = vals[k] / Fraction(2) ** int(e[m])
+            assert float(x16[m, k]) == _rt16(sv)
+        assert max(abs(v) for v in vals) <= Fraction(2) ** int(e[m]) < 2 * max(abs(v) for v in vals)
+
+
+def test_linear_w8a16_rs_equals_w8a16_in_range():
+    rng = np.random.default_rng(43)
+    x = rng.integers(-8, 9, (5, 512)).astype(np.float16)
+    w = rng.normal(0, 0.02, (7, 512)).astype(np.float32)
+    qw, sw = O.quantize_weights(w)
+    b = rng.normal(0, 0.1, 7).astype(np.float32)
+    a = O.linear_w8a16_rs(x.astype(np.float32), qw, sw, bias=b, out="f16")
+    ref = O.linear_w8a16(x, qw, sw, b)
+    assert np.array_equal(a.view(np.uint16), ref.view(np.uint16))
+
+
+def test_linear_w8a16_rs_near_max_inputs_finite_and_accurate():
+    # rows of +-65504 overflow the plain weight-only path's fp16 rotation; the
+    # range-safe path stays finite and close to the float64 product
+    rng = np.random.default_rng(44)
+    x = (np.sign(rng.normal(0, 1, (4, 256))) * 65504).astype(np.float32)
+    w = rng.normal(0, 0.02, (6, 256)).astype(np.float32)
+    qw, sw = O.quantize_weights(w)
+    plain = O.linear_w8a16(x.astype(np.float16), qw, sw).astype(np.float64)
+    assert not np.isfinite(plain).all()
+    rs = O.linear_w8a16_rs(x, qw, sw, out="bf16").astype(np.float64)
+    truth = x.astype(np.float64) @ O.dequantize_weights(qw, sw).astype(np.float64).T
+    assert np.isfinite(rs).all()
+    assert np.linalg.norm(rs - truth) <= 1e-2 * np.linalg.norm(truth)
