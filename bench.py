@@ -308,12 +308,14 @@ def main():
         ws16 = torch.empty(cr.workspace_bytes(cr.PATH_W8A16, M, N, K, wl.LORA_RANK), dtype=torch.uint8, device=dev)
         ws8l = torch.empty(cr.workspace_bytes(cr.PATH_W8A8, M, N, K, wl.LORA_RANK), dtype=torch.uint8, device=dev)
         wsd = torch.empty(cr.workspace_bytes(cr.PATH_DEQUANT, M, N, K), dtype=torch.uint8, device=dev)
+        wsr = torch.empty(cr.workspace_bytes(cr.PATH_W8A16_RS, M, N, K), dtype=torch.uint8, device=dev)
         down, up = wl.make_lora(N, K, seed=0)
         # Q_X / s_X of the stand-alone prologue and GEMM legs
         qx = torch.empty((M, K), dtype=torch.int8, device=dev)
         sx = torch.empty(M, dtype=torch.float32, device=dev)
         per_shape.append(dict(N=N, K=K, layers=layers, x=x, qws=qws, sw=sw, w16=w16, y=y, ws8=ws8,
-                              ws8l=ws8l, wsd=wsd, ws16=ws16, down=down.to(dev), up=up.to(dev), qx=qx, sx=sx,
+                              ws8l=ws8l, wsd=wsd, wsr=wsr, ws16=ws16, xb=x.to(torch.bfloat16),
+                              yb=torch.empty((M, N), dtype=torch.bfloat16, device=dev), down=down.to(dev), up=up.to(dev), qx=qx, sx=sx,
                               bias=wl.make_bias(N, seed=0).to(dev), res=wl.make_residual(M, N, seed=0).to(dev)))
     torch.cuda.synchronize()
     ops_step = sum(2.0 * M * s["N"] * s["K"] * s["layers"] for s in per_shape)
@@ -440,8 +442,8 @@ def main():
 
         compare = {}
         if not args.no_compare:
-            log("comparison sweeps: W8A8 with bias/residual/LoRA, W8A16+LoRA, dequantise-every-call, "
-                "own fp16 GEMM, torch F.linear")
+            log("comparison sweeps: W8A8 with bias/residual/LoRA, W8A16+LoRA, range-safe W8A16 (bf16), "
+                "dequantise-every-call, own fp16 GEMM, torch F.linear")
             def w8a16_step():
                 for s in per_shape:
                     for q in s["qws"]:
@@ -464,6 +466,11 @@ def main():
                     for q in s["qws"]:
                         cr.linear_dequant(s["x"], q, s["sw"], workspace=s["wsd"])
 
+            def w8a16_rs_step():
+                for s in per_shape:
+                    for q in s["qws"]:
+                        cr.linear_w8a16_rs(s["xb"], q, s["sw"], out=s["yb"], workspace=s["wsr"])
+
             def own_f16_step():
                 h = torch.cuda.current_stream().cuda_stream
                 for s in per_shape:
@@ -478,7 +485,8 @@ def main():
 
             for name, fn in (("w8a8_bias_residual", w8a8_bias_res_step),
                              ("w8a8_lora32_bias_residual", w8a8_lora_step),
-                             ("w8a16_lora32", w8a16_step), ("dequant_every_call", dequant_step),
+                             ("w8a16_lora32", w8a16_step), ("w8a16_rangesafe_bf16", w8a16_rs_step),
+                             ("dequant_every_call", dequant_step),
                              ("fp16_own_mfma", own_f16_step),
                              ("fp16_torch_linear", torch_f16_step)):
                 gc = capture(fn, stream)

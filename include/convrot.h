@@ -71,8 +71,15 @@ typedef enum convrot_status {
 typedef enum convrot_path {
   CONVROT_PATH_W8A8 = 0,
   CONVROT_PATH_W8A16 = 1,
-  CONVROT_PATH_DEQUANT = 2
+  CONVROT_PATH_DEQUANT = 2,
+  CONVROT_PATH_W8A16_RS = 3
 } convrot_path;
+
+/* 16-bit floating-point formats of the range-safe weight-only path. */
+typedef enum convrot_dtype {
+  CONVROT_DTYPE_F16 = 0,  /* IEEE binary16 */
+  CONVROT_DTYPE_BF16 = 1  /* bfloat16: the upper half of an IEEE binary32 */
+} convrot_dtype;
 
 /* Unmerged LoRA of the int8 linears.  Page "[PR #249] Add an mps
  * backend: weight-only INT8 and W4A8/W6A8 linears for Apple GPUs", sections
@@ -165,7 +172,31 @@ convrot_status convrot_linear_dequant(const void* X, int64_t M, int64_t K,
                                       const float* bias, void* Y,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* The range-safe weight-only linear: page "[PR #249] Add an mps backend
+ * ...", section "Design" (range safety by construction).  X [M, K] is fp16 or
+ * bf16 (x_dtype); each row is rotated (exact fp64 transform; for bf16 rows
+ * exact while a group's values span at most 45 binades) and divided by 2^e,
+ * e the smallest integer with max |X H| <= 2^e (0 for a zero row), before the
+ * one rounding to fp16, so no row can overflow fp16 whatever its range; the
+ * workspace holds that fp16 activation [M, K] and e [M] (int32).  The fp16
+ * MFMA accumulates in fp32 (no K limit), the epilogue restores 2^e exactly
+ * (ldexp), multiplies by s_W, adds the optional bias and rounds once to
+ * y_dtype (fp16 or bf16, round to nearest even); an optional residual of
+ * y_dtype [M, N] (which may be Y itself) is then added as one addition in
+ * y_dtype.  Y matches the exact value within accumulation error.  Workspace:
+ * convrot_workspace_bytes(CONVROT_PATH_W8A16_RS, M, N, K, 0).  A dtype other
+ * than the two above is CONVROT_ERR_INVALID_ARG. */
+convrot_status convrot_linear_w8a16_rs(const void* X, int x_dtype, int64_t M, int64_t K,
+                                       const int8_t* Q_W, const float* s_W, int64_t N,
+                                       const float* bias, const void* residual, void* Y, int y_dtype,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- stages (exported for parity tests and per-kernel measurement) ---- */
+
+/* The range-safe prologue alone: X fp16 or bf16 [M, K] -> X16 fp16 [M, K] =
+ * fp16(X H 2^-e) (rounded once) and e int32 [M]. */
+convrot_status convrot_act_rotate_scaled(const void* X, int x_dtype, int64_t M, int64_t K,
+                                         void* X16, int32_t* rowexp, void* stream);
 
 /* The baseline's weight step alone: Q_W int8 [N, K], s_W fp32 [N] ->
  * W16 fp16 [N, K] = fp16((Q_W (.) s_W) H), correctly rounded. */

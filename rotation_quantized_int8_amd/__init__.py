@@ -7,8 +7,8 @@ There is no CPU fallback: if the library is missing or the device is not
 gfx950, the calls raise.
 
 Functions mirror the C entry points:
-  quantize_weights, linear_w8a8, linear_w8a8_ex, linear_w8a16, linear_dequant,
-  dequantize_weights, act_quant, act_rotate_f16,
+  quantize_weights, linear_w8a8, linear_w8a8_ex, linear_w8a16, linear_w8a16_rs,
+  linear_dequant, dequantize_weights, act_quant, act_rotate_f16, act_rotate_scaled,
   gemm_i8_i32, gemm_i8_f16, gemm_f16, workspace_bytes.
 """
 
@@ -28,6 +28,9 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG_DIR), "include", "convrot.h")
 PATH_W8A8 = 0
 PATH_W8A16 = 1
 PATH_DEQUANT = 2
+PATH_W8A16_RS = 3
+DTYPE_F16 = 0
+DTYPE_BF16 = 1
 GROUP = 256
 K_MAX = 131072
 LORA_RANK_MAX = 64
@@ -51,6 +54,9 @@ _SIGNATURES = {
                                             ctypes.POINTER(_Lora), _vp, _vp, _sz, _vp]),
     "convrot_linear_dequant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "convrot_dequantize_weights": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "convrot_linear_w8a16_rs": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
+                                               ctypes.c_int, _vp, _sz, _vp]),
+    "convrot_act_rotate_scaled": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _vp]),
     "convrot_act_quant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "convrot_act_rotate_f16": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "convrot_gemm_i8_i32": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -286,6 +292,66 @@ def linear_dequant(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
                                             _ptr(y), _ptr(ws), nbytes, _stream(x2)),
                "convrot_linear_dequant")
     return y.reshape(*lead, N)
+
+
+_DTYPES = {torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
+
+
+def _prep16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be a float16 or bfloat16 tensor")
+    return _prep(t, t.dtype, name)
+
+
+def linear_w8a16_rs(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
+                    bias: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Range-safe weight-only linear: x fp16/bf16 [..., K] -> out_dtype [..., N]
+    (default x.dtype), optional bias and residual (out_dtype, may be ``out``)."""
+    x2, lead = _flatten(_prep16(x, "x"))
+    out_dtype = out_dtype or x.dtype
+    if out_dtype not in _DTYPES:
+        raise TypeError("out_dtype must be float16 or bfloat16")
+    q_w = _prep(q_w, torch.int8, "Q_W")
+    s_w = _prep(s_w, torch.float32, "s_W")
+    bias = None if bias is None else _prep(bias, torch.float32, "bias")
+    M, K = x2.shape
+    N = q_w.shape[0]
+    if q_w.shape[1] != K:
+        raise ValueError(f"Q_W has K={q_w.shape[1]}, x has K={K}")
+    if out is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        if out.dtype != out_dtype or not out.is_contiguous() or out.numel() != M * N:
+            raise ValueError("out must be a contiguous tensor of out_dtype with M * N elements")
+        y = out.view(M, N)
+    res = None
+    if residual is not None:
+        if residual.dtype != out_dtype or residual.numel() != M * N:
+            raise ValueError("residual must have out_dtype and M * N elements")
+        if out is not None and residual.data_ptr() == out.data_ptr() and residual.is_contiguous():
+            res = y
+        else:
+            res = _prep(residual, out_dtype, "residual").view(M, N)
+    ws, nbytes = _workspace(PATH_W8A16_RS, M, N, K, 0, x.device, workspace)
+    with torch.cuda.device(x.device):
+        _check(lib().convrot_linear_w8a16_rs(_ptr(x2), _DTYPES[x2.dtype], M, K, _ptr(q_w), _ptr(s_w), N,
+                                             _ptr(bias), _ptr(res), _ptr(y), _DTYPES[out_dtype], _ptr(ws),
+                                             nbytes, _stream(x2)), "convrot_linear_w8a16_rs")
+    return y.reshape(*lead, N)
+
+
+def act_rotate_scaled(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Range-safe prologue alone: x fp16/bf16 [M, K] -> (fp16(x H 2^-e) [M, K], e int32 [M])."""
+    x = _prep16(x, "x")
+    M, K = x.shape
+    out = torch.empty((M, K), dtype=torch.float16, device=x.device)
+    e = torch.empty((M,), dtype=torch.int32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().convrot_act_rotate_scaled(_ptr(x), _DTYPES[x.dtype], M, K, _ptr(out), _ptr(e), _stream(x)),
+               "convrot_act_rotate_scaled")
+    return out, e
 
 
 def act_quant(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -110,6 +110,8 @@ size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_
   }
   if (path == CONVROT_PATH_W8A16) return round256((size_t)M * K * 2) + lora_ws_bytes(M, N, K, lora_rank);
   if (path == CONVROT_PATH_DEQUANT) return lora_rank == 0 ? round256((size_t)N * K * 2) : (size_t)-1;
+  if (path == CONVROT_PATH_W8A16_RS)
+    return lora_rank == 0 ? round256((size_t)M * K * 2) + round256((size_t)M * 4) : (size_t)-1;
   return (size_t)-1;
 }
 
@@ -360,6 +362,60 @@ convrot_status convrot_linear_dequant(const void* X, int64_t M, int64_t K, const
   GemmArgs g{};
   g.X = X; g.W = workspace; g.bias = bias; g.out = Y; g.M = M; g.N = N; g.K = K;
   return launched(launch_gemm<GemmMode::kF16>(g, s));
+}
+
+convrot_status convrot_act_rotate_scaled(const void* X, int x_dtype, int64_t M, int64_t K, void* X16,
+                                         int32_t* rowexp, void* stream) {
+  if (M < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (x_dtype != CONVROT_DTYPE_F16 && x_dtype != CONVROT_DTYPE_BF16) return CONVROT_ERR_INVALID_ARG;
+  if (M == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!X || !X16 || !rowexp) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(X16) || !aligned16(rowexp)) return CONVROT_ERR_ALIGNMENT;
+  const size_t xb = (size_t)M * K * 2, eb = (size_t)M * 4;
+  if (overlap(X16, xb, X, xb) || overlap(rowexp, eb, X, xb) || overlap(rowexp, eb, X16, xb))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  return launched(launch_act_rotate_scaled(X, x_dtype == CONVROT_DTYPE_BF16, M, K, X16, rowexp, as_stream(stream)));
+}
+
+convrot_status convrot_linear_w8a16_rs(const void* X, int x_dtype, int64_t M, int64_t K, const int8_t* Q_W,
+                                       const float* s_W, int64_t N, const float* bias, const void* residual,
+                                       void* Y, int y_dtype, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if ((x_dtype != CONVROT_DTYPE_F16 && x_dtype != CONVROT_DTYPE_BF16) ||
+      (y_dtype != CONVROT_DTYPE_F16 && y_dtype != CONVROT_DTYPE_BF16))
+    return CONVROT_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
+      (bias && !aligned16(bias)) || (residual && !aligned16(residual)) || (workspace && !aligned16(workspace)))
+    return CONVROT_ERR_ALIGNMENT;
+  const size_t need = convrot_workspace_bytes(CONVROT_PATH_W8A16_RS, M, N, K, 0);
+  if (!workspace || workspace_bytes < need) return CONVROT_ERR_WORKSPACE;
+  const size_t yb = (size_t)M * N * 2, xb = (size_t)M * K * 2, qb = (size_t)N * K, sb = (size_t)N * 4;
+  const size_t bb = bias ? (size_t)N * 4 : 0, rb = residual ? yb : 0;
+  if (overlap(Y, yb, X, xb) || overlap(Y, yb, Q_W, qb) || overlap(Y, yb, s_W, sb) || overlap(Y, yb, bias, bb) ||
+      overlap(Y, yb, workspace, need) || (residual != Y && overlap(Y, yb, residual, rb)) ||
+      overlap(workspace, need, X, xb) || overlap(workspace, need, Q_W, qb) || overlap(workspace, need, s_W, sb) ||
+      overlap(workspace, need, bias, bb) || overlap(workspace, need, residual, rb))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  hipStream_t s = as_stream(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  void* X16 = ws;
+  int* rowexp = reinterpret_cast<int*>(ws + round256((size_t)M * K * 2));
+  if (convrot_status st =
+          launched(launch_act_rotate_scaled(X, x_dtype == CONVROT_DTYPE_BF16, M, K, X16, rowexp, s)))
+    return st;
+  GemmArgs g{};
+  g.X = X16; g.W = Q_W; g.sW = s_W; g.bias = bias; g.out = Y;
+  g.R = reinterpret_cast<const __half*>(residual);
+  g.rowexp = rowexp; g.out_bf16 = y_dtype == CONVROT_DTYPE_BF16;
+  g.M = M; g.N = N; g.K = K;
+  return launched(launch_gemm<GemmMode::kW8A16>(g, s));
 }
 
 convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const int8_t* Q_W,

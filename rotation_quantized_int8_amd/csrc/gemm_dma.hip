@@ -121,6 +121,26 @@ __device__ __forceinline__ v8h lora_frag(const __half* __restrict__ base, int64_
   return *reinterpret_cast<const v8h*>(&v);
 }
 
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN), and back.
+__device__ __forceinline__ uint16_t f32_to_bf16_rn(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Eight bf16 additions, each rounded once: a + b in fp32 (fp32 carries more
+// than twice bf16's precision, so this is the correctly rounded bf16 sum).
+__device__ __forceinline__ v4i add_bf16x8(v4i a, v4i b) {
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(&a);
+  const uint16_t* y = reinterpret_cast<const uint16_t*>(&b);
+  uint16_t z[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = f32_to_bf16_rn(bf16_to_f32(x[e]) + bf16_to_f32(y[e]));
+  return *reinterpret_cast<const v4i*>(z);
+}
+
 // Eight fp16 additions, each rounded once: a + b in fp32, then to fp16.
 __device__ __forceinline__ v4i add_f16x8(v4i a, v4i b) {
   const __half* x = reinterpret_cast<const __half*>(&a);
@@ -200,6 +220,14 @@ gemm_dma_kernel(GemmArgs p) {
   const int orow = lane & 15;        // output row within a fragment
   const int ocol = (lane >> 4) * 4;  // first of 4 output columns within a fragment
   float sxv[FM], swv[FN][4], bsv[FN][4];
+  int rexp[FM];   // range-safe weight-only: per-row power of two to restore
+  if constexpr (kW16 && EXTRA) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t m = m0 + wm * WM + j * 16 + orow;
+      rexp[j] = p.rowexp ? p.rowexp[m < M ? m : M - 1] : 0;
+    }
+  }
   if constexpr (MODE == GemmMode::kI8toF16) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
@@ -442,7 +470,7 @@ gemm_dma_kernel(GemmArgs p) {
 
   // W8A8 residual: the whole-chunk parts this thread will add are fetched now,
   // so that their latency hides behind the epilogue arithmetic.
-  constexpr bool kRes = (MODE == GemmMode::kI8toF16) && EXTRA;
+  constexpr bool kRes = (MODE == GemmMode::kI8toF16 || kW16) && EXTRA;
   const __half* res = kRes ? p.R : nullptr;
   v4i rres[kRes ? CPT : 1];
   if constexpr (kRes) {
@@ -483,7 +511,11 @@ gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < FM; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yf[i][j][r] = __fmul_rn(acc[i][j][r], swv[i][r]);
+        for (int r = 0; r < 4; ++r) {
+          float y = __fmul_rn(acc[i][j][r], swv[i][r]);
+          if constexpr (EXTRA) y = ldexpf(y, rexp[j]);   // exact power-of-two restore
+          yf[i][j][r] = y;
+        }
   }
   if constexpr (kLora) {
     if (p.t_ld > 0) lora_mma(yf);
@@ -515,7 +547,7 @@ gemm_dma_kernel(GemmArgs p) {
           for (int r = 0; r < 4; ++r) {
             float y = yf[i][j][r];
             if (p.bias) y = __fadd_rn(y, bsv[i][r]);
-            h[r] = __float2half_rn(y);
+            h[r] = EXTRA && p.out_bf16 ? __ushort_as_half(f32_to_bf16_rn(y)) : __float2half_rn(y);
           }
         } else {
 #pragma unroll
@@ -548,7 +580,7 @@ gemm_dma_kernel(GemmArgs p) {
     if (vec_rows && n + 16 / kOut <= N) {
       v4i v = *reinterpret_cast<const v4i*>(sp);
       if constexpr (kRes) {
-        if (res) v = add_f16x8(v, rres[q]);
+        if (res) v = p.out_bf16 ? add_bf16x8(v, rres[q]) : add_f16x8(v, rres[q]);
       }
       // streaming store: the output is not re-read by this kernel
       __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(gp));
@@ -558,7 +590,14 @@ gemm_dma_kernel(GemmArgs p) {
         if (n + e >= N) continue;
         OutT o = reinterpret_cast<const OutT*>(sp)[e];
         if constexpr (kRes) {
-          if (res) o = __float2half_rn(__half2float(o) + __half2float(res[m * N + n + e]));
+          if (res) {
+            if (p.out_bf16) {
+              const float sum = bf16_to_f32(__half_as_ushort(o)) + bf16_to_f32(__half_as_ushort(res[m * N + n + e]));
+              o = __ushort_as_half(f32_to_bf16_rn(sum));
+            } else {
+              o = __float2half_rn(__half2float(o) + __half2float(res[m * N + n + e]));
+            }
+          }
         }
         reinterpret_cast<OutT*>(gp)[e] = o;
       }
@@ -594,7 +633,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 template <GemmMode MODE>
 hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
   if constexpr (MODE == GemmMode::kI8toF16 || MODE == GemmMode::kW8A16) {
-    if (a.R || a.t_ld > 0) {
+    if (a.R || a.t_ld > 0 || a.rowexp || a.out_bf16) {
       switch (cfg) {
         case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4, true>(a, stream);
         case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4, true>(a, stream);

@@ -17,6 +17,8 @@ struct GemmArgs {
   const __half* T;      // [M, t_ld] fp16 LoRA activation X down^T (kI8toF16, kW8A16)
   const __half* U;      // [N, t_ld] fp16 LoRA up weight U' = fp16(scale * up), zero past the rank
   int t_ld;             // LoRA rank rounded up to 32 (0 = no LoRA)
+  const int* rowexp;    // [M] power of two per row to restore (range-safe kW8A16), or null
+  int out_bf16;         // kW8A16: output (and residual) bf16 instead of fp16
   void* out;            // [M, N] int32 or fp16; with kc: [K / kc, M, N] int32 partials
   int64_t M, N, K;
   int64_t kc;           // 0, or K per split (kI8toI32 only; a multiple of 256 dividing K)
@@ -69,6 +71,9 @@ hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, flo
                             hipStream_t stream);
 hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
                                  hipStream_t stream);
+// Range-safe weight-only prologue: X fp16 or bf16 [M, K] -> X16 = fp16(X H 2^-e) and e [M].
+hipError_t launch_act_rotate_scaled(const void* X, bool bf16, int64_t M, int64_t K, void* X16,
+                                    int* rowexp, hipStream_t stream);
 
 // LoRA operands of the GEMM epilogue: T fp16 [M, t_ld] = X down^T and
 // U' fp16 [N, t_ld] = fp16(scale * up) (columns past the rank zero).  K is

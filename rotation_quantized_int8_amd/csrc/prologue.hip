@@ -1,9 +1,13 @@
 // Activation prologue: X_rot = X H per 256-group, s_X = row max / 127,
-// Q_X = round(X_rot / s_X) -- or, for the weight-only path, X16 = fp16(X H).
+// Q_X = round(X_rot / s_X) -- or, for the weight-only path, X16 = fp16(X H),
+// or, range-safe, X16 = fp16(X H 2^-e) with a power of two per row.
 //
 // Page "INT8ConvRot GEMM vs fp16 on M1 Max with Metal, MPSMatrix, and MLX
 // (fp16 Wins)", section "What changed in the computation": activation
-// equation (every call) and the weight-only listing (x_rot kept in fp16).
+// equation (every call) and the weight-only listing (x_rot kept in fp16);
+// page "[PR #249] Add an mps backend ...", section "Design": the range-safe
+// prologue divides each row by an exact power of two so that its rotated
+// maximum is at most 1.
 //
 // The rotation (exact fp64 butterflies, one rounding) and the quantisation
 // are the device functions of rotate.hpp.
@@ -25,12 +29,28 @@ struct Split {
   int chunks;        // chunks per row
 };
 
-template <bool kInt8>
+enum PrologueMode { kQuantInt8 = 0, kRotateF16 = 1, kRotateScaledF16 = 2 };
+
+// Row maximum of non-negative doubles across 16-lane segments: the bit
+// patterns of non-negative doubles order like unsigned integers.
+__device__ __forceinline__ double seg_max_f64(double v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v = fmax(v, __shfl_xor(v, m));
+  return v;
+}
+
+// kQuantInt8: Q_X, s_X.  kRotateF16: X16 = fp16(X H).  kRotateScaledF16 (range
+// safe, [P4] "Design"): X16 = fp16(X H 2^-e) with e the smallest integer such
+// that the row's max |X H| <= 2^e (0 for a zero row), and e per row.  kBF16:
+// the input is bf16 (kRotateScaledF16 only).
+template <int kMode, bool kBF16>
 __global__ void __launch_bounds__(1024)
-prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
-                int8_t* __restrict__ QX, float* __restrict__ sX, __half* __restrict__ X16) {
+prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
+                int8_t* __restrict__ QX, float* __restrict__ sX, __half* __restrict__ X16,
+                int* __restrict__ rowexp) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ uint32_t rowmax[16];   // per row: max |X_rot| as fp32 bits (non-negative: uint order)
+  __shared__ uint32_t rowmax[16];             // per row: max |X_rot| as fp32 bits (non-negative: uint order)
+  __shared__ unsigned long long rowmax64[16]; // the same as fp64 bits (row-scaled mode)
 
   const int tid = threadIdx.x;
   const int slot_id = tid >> 4;     // group slot in the workgroup
@@ -42,18 +62,19 @@ prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
   const bool active = row_in_wg < sp.rows_per_wg && row < M;
   char* slot = smem + slot_id * kSlotBytes;
 
-  const __half* xrow = X + row * K;
+  const uint16_t* xrow = X + row * K;
   double y[16];
   float f[16];
 
-  if (kInt8 && tid < 16) rowmax[tid] = 0u;
-  if (!kInt8) {
+  if (kMode == kQuantInt8 && tid < 16) rowmax[tid] = 0u;
+  if (kMode == kRotateScaledF16 && tid < 16) rowmax64[tid] = 0ull;
+  if constexpr (kMode == kRotateF16) {
     // Weight-only path: no row scale, just fp16(X H) per group.
     if (active) {
       for (int c = 0; c < sp.chunks; ++c) {
         const int g = c * sp.gpc + gi;
         if (g >= G) break;
-        rotate_group(xrow + (int64_t)g * kGroup, slot, lane, y);
+        rotate_group<kBF16>(xrow + (int64_t)g * kGroup, slot, lane, y);
         __half h[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) h[i] = f64_to_f16_rn(y[i] * 0.0625);
@@ -65,6 +86,47 @@ prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
     return;
   }
 
+  if constexpr (kMode == kRotateScaledF16) {
+    __syncthreads();   // rowmax64 cleared
+    // pass 1: transform, keep the values when the row fits in one chunk, take max
+    double amax = 0.0;
+    if (active) {
+      for (int c = 0; c < sp.chunks; ++c) {
+        const int g = c * sp.gpc + gi;
+        if (g >= G) break;
+        rotate_group<kBF16>(xrow + (int64_t)g * kGroup, slot, lane, y);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmax(amax, fabs(y[i] * 0.0625));
+      }
+    }
+    amax = seg_max_f64(amax);
+    if (active && lane == 0) atomicMax(&rowmax64[row_in_wg], (unsigned long long)__double_as_longlong(amax));
+    __syncthreads();
+    if (!active) return;
+    // e: max = 1.f 2^ex (normal double) -> e = ex, or ex + 1 when f > 0
+    const unsigned long long mb = rowmax64[row_in_wg];
+    int e = 0;
+    if (mb != 0ull) {
+      const int ex = (int)((mb >> 52) & 0x7FF) - 1023;
+      e = (mb & ((1ull << 52) - 1)) == 0ull ? ex : ex + 1;
+    }
+    const double down = ldexp(0.0625, -e);   // exact power of two
+    if (slot_id == row_in_wg * sp.gpc && lane == 0) rowexp[row] = e;
+    // pass 2: scale, round once to fp16, store
+    for (int c = 0; c < sp.chunks; ++c) {
+      const int g = c * sp.gpc + gi;
+      if (g >= G) break;
+      if (sp.chunks > 1) rotate_group<kBF16>(xrow + (int64_t)g * kGroup, slot, lane, y);
+      __half h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[i] = f64_to_f16_rn(y[i] * down);
+      uint4* dst = reinterpret_cast<uint4*>(X16 + row * K + (int64_t)g * kGroup + 16 * lane);
+      dst[0] = *reinterpret_cast<const uint4*>(&h[0]);
+      dst[1] = *reinterpret_cast<const uint4*>(&h[8]);
+    }
+    return;
+  }
+
   __syncthreads();   // rowmax cleared
   // pass 1: transform, keep the values when the row fits in one chunk, take max
   float amax = 0.0f;
@@ -72,7 +134,7 @@ prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
     for (int c = 0; c < sp.chunks; ++c) {
       const int g = c * sp.gpc + gi;
       if (g >= G) break;
-      rotate_group(xrow + (int64_t)g * kGroup, slot, lane, y);
+      rotate_group<kBF16>(xrow + (int64_t)g * kGroup, slot, lane, y);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         f[i] = (float)(y[i] * 0.0625);  // exact scaling, single rounding to fp32
@@ -93,7 +155,7 @@ prologue_kernel(const __half* __restrict__ X, int64_t M, int64_t K, Split sp,
     const int g = c * sp.gpc + gi;
     if (g >= G) break;
     if (sp.chunks > 1) {
-      rotate_group(xrow + (int64_t)g * kGroup, slot, lane, y);
+      rotate_group<kBF16>(xrow + (int64_t)g * kGroup, slot, lane, y);
 #pragma unroll
       for (int i = 0; i < 16; ++i) f[i] = (float)(y[i] * 0.0625);
     }
@@ -121,21 +183,22 @@ Split choose_split(int64_t K) {
   return sp;
 }
 
-template <bool kInt8>
-hipError_t launch(const __half* X, int64_t M, int64_t K, int8_t* QX, float* sX, __half* X16,
+template <int kMode, bool kBF16>
+hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __half* X16, int* rowexp,
                   hipStream_t stream) {
   const Split sp = choose_split(K);
   const int slots = sp.rows_per_wg * sp.gpc;
   const int threads = ((slots * 16 + 63) / 64) * 64;
   const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
   const size_t lds = (size_t)(threads / 16) * kSlotBytes;
+  auto fn = &prologue_kernel<kMode, kBF16>;
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prologue_kernel<kInt8>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(prologue_kernel<kInt8>, dim3((unsigned)blocks), dim3(threads), lds, stream,
-                     X, M, K, sp, QX, sX, X16);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), lds, stream,
+                     reinterpret_cast<const uint16_t*>(X), M, K, sp, QX, sX, X16, rowexp);
   return hipGetLastError();
 }
 
@@ -143,13 +206,22 @@ hipError_t launch(const __half* X, int64_t M, int64_t K, int8_t* QX, float* sX, 
 
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
                             hipStream_t stream) {
-  return launch<true>(reinterpret_cast<const __half*>(X), M, K, QX, sX, nullptr, stream);
+  return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream);
 }
 
 hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
                                  hipStream_t stream) {
-  return launch<false>(reinterpret_cast<const __half*>(X), M, K, nullptr, nullptr,
-                       reinterpret_cast<__half*>(X16), stream);
+  return launch<kRotateF16, false>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), nullptr,
+                                   stream);
+}
+
+hipError_t launch_act_rotate_scaled(const void* X, bool bf16, int64_t M, int64_t K, void* X16,
+                                    int* rowexp, hipStream_t stream) {
+  if (bf16)
+    return launch<kRotateScaledF16, true>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), rowexp,
+                                          stream);
+  return launch<kRotateScaledF16, false>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), rowexp,
+                                         stream);
 }
 
 }  // namespace convrot

@@ -46,20 +46,31 @@ __device__ __forceinline__ void fwht16(double (&v)[16]) {
   }
 }
 
+// One 16-bit input value as a double: fp16, or bf16 (the upper half of an fp32).
+template <bool kBF16>
+__device__ __forceinline__ double in16_to_f64(uint16_t bits) {
+  if constexpr (kBF16) return (double)__uint_as_float((uint32_t)bits << 16);
+  else return (double)__half2float(__ushort_as_half(bits));
+}
+
 // Steps 1-4 for one group whose row `lane` (elements 16 lane .. 16 lane + 15)
-// this lane already holds as two 16-byte halves r0, r1.  On return y[] holds
-// the exact outputs 16 * x_rot of the same row of the group.  `slot` is the
-// segment's private LDS slot (kSlotBytes); it is free again on return.
+// this lane already holds as two 16-byte halves r0, r1 of 16-bit values (fp16,
+// or bf16 with kBF16).  On return y[] holds 16 * x_rot of the same row of the
+// group: exact for fp16 inputs, and for bf16 inputs whenever the group's
+// values span at most 45 binades (every partial sum then fits 53 bits).
+// `slot` is the segment's private LDS slot (kSlotBytes); it is free again on
+// return.
+template <bool kBF16 = false>
 __device__ __forceinline__ void rotate_loaded(v4i r0, v4i r1, char* slot, int lane, double (&y)[16]) {
   v4i* st = reinterpret_cast<v4i*>(slot + 32 * lane);
   st[0] = r0;
   st[1] = r1;
   wave_lds_sync();
   // column `lane`: element (a, lane) for a = 0..15
-  const __half* sh = reinterpret_cast<const __half*>(slot);
+  const uint16_t* sh = reinterpret_cast<const uint16_t*>(slot);
   double v[16];
 #pragma unroll
-  for (int a = 0; a < 16; ++a) v[a] = (double)__half2float(sh[16 * a + lane]);
+  for (int a = 0; a < 16; ++a) v[a] = in16_to_f64<kBF16>(sh[16 * a + lane]);
   wave_lds_sync();  // all staging reads done before the slot is reused below
   fwht16(v);        // along a: v[c] = Z[c][lane]
   // transpose: Z[c][b] at row c, 16-byte chunk (b >> 1) ^ (c & 7)
@@ -79,12 +90,17 @@ __device__ __forceinline__ void rotate_loaded(v4i r0, v4i r1, char* slot, int la
 }
 
 // Loads row `lane` of the group at `src` and rotates it (see rotate_loaded).
-__device__ __forceinline__ void rotate_group(const __half* __restrict__ src, char* slot, int lane,
+template <bool kBF16 = false>
+__device__ __forceinline__ void rotate_group(const uint16_t* __restrict__ src, char* slot, int lane,
                                              double (&y)[16]) {
   const v4i* s4 = reinterpret_cast<const v4i*>(src + 16 * lane);
   const v4i r0 = __builtin_nontemporal_load(s4);
   const v4i r1 = __builtin_nontemporal_load(s4 + 1);
-  rotate_loaded(r0, r1, slot, lane, y);
+  rotate_loaded<kBF16>(r0, r1, slot, lane, y);
+}
+__device__ __forceinline__ void rotate_group(const __half* __restrict__ src, char* slot, int lane,
+                                             double (&y)[16]) {
+  rotate_group<false>(reinterpret_cast<const uint16_t*>(src), slot, lane, y);
 }
 
 // Exact-definition quantisation of 16 fp32 values with scale s (> 0):

@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = cr.header_functions()
-    assert len(declared) == 14
+    assert len(declared) == 16
     for name in declared:
         assert hasattr(L, name), name
     assert set(declared) == set(cr._SIGNATURES)
@@ -65,6 +65,9 @@ def test_workspace_bytes(L):
     # dequantise-every-call: the fp16 weight [N, K]
     assert L.convrot_workspace_bytes(2, 4, 8, 256, 0) == 8 * 256 * 2
     assert L.convrot_workspace_bytes(2, 4, 8, 256, 4) == bad
+    # range-safe weight-only: fp16 activation [M, K] and the row exponents [M]
+    assert L.convrot_workspace_bytes(3, 4, 8, 256, 0) == 2048 + 256
+    assert L.convrot_workspace_bytes(3, 4, 8, 256, 1) == bad
 
 
 P = 1 << 20          # a fake, 16-byte aligned "device" address: never dereferenced
@@ -160,6 +163,25 @@ def test_dequant_argument_errors(L):
     assert d(P, Q, 8, 256, None, None) == INVALID
     assert d(P, Q, 8, 256, P + 16, None) == INVALID
     assert d(P, Q + 4, 8, 256, R, None) == ALIGN
+
+
+def test_w8a16_rs_argument_errors(L):
+    f = L.convrot_linear_w8a16_rs
+    ws = L.convrot_workspace_bytes(3, 4, 8, 256, 0)
+    Y, W = S, S + 4096
+    assert f(None, 0, 0, 256, None, None, 8, None, None, None, 0, None, 0, None) == OK
+    assert f(P, 2, 4, 256, Q, R, 8, None, None, Y, 0, W, ws, None) == INVALID        # bad x dtype
+    assert f(P, 0, 4, 256, Q, R, 8, None, None, Y, 5, W, ws, None) == INVALID        # bad y dtype
+    assert f(P, 1, 4, 300, Q, R, 8, None, None, Y, 1, W, ws, None) == SHAPE
+    assert f(P, 1, 4, 256, Q, R, 8, None, Y + 8, Y, 1, W, ws, None) == ALIGN         # residual alignment
+    assert f(P, 1, 4, 256, Q, R, 8, None, Y + 16, Y, 1, W, ws, None) == INVALID      # residual overlaps Y
+    assert f(P, 1, 4, 256, Q, R, 8, None, None, Y, 1, W, ws - 1, None) == WORKSPACE
+    assert f(P, 1, 4, 256, Q, R, 8, None, None, W, 1, W, ws, None) == INVALID        # Y in the workspace
+    a = L.convrot_act_rotate_scaled
+    assert a(P, 3, 4, 256, Q, R, None) == INVALID
+    assert a(P, 1, 4, 255, Q, R, None) == SHAPE
+    assert a(P, 1, 4, 256, Q, R + 4, None) == ALIGN
+    assert a(P, 1, 4, 256, P + 512, R, None) == INVALID
 
 
 def test_stage_argument_errors(L):

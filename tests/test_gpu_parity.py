@@ -617,3 +617,74 @@ def test_linear_w8a8_ex_few_rows(M, N, K, rank):
     else:
         d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
         assert int((d > tol).sum()) == 0
+
+
+# ------------------------------------ range-safe weight-only path (next-3)
+
+def _rs_input(M, K, dtype, kind, seed):
+    """float32 values representable in the 16-bit input type, and that tensor."""
+    g = torch.Generator().manual_seed(seed)
+    if kind == "normal":
+        v = wl.make_activations(M, K, seed=seed).float()
+    elif kind == "huge":
+        v = torch.randn((M, K), generator=g) * 1e30
+    elif kind == "nearmax":
+        v = torch.sign(torch.randn((M, K), generator=g)) * 65504.0
+        v[1::2] = torch.randn((M // 2, K), generator=g) * 3.0
+    else:   # zero row, a row of tiny values, a normal row
+        v = torch.randn((M, K), generator=g)
+        v[0] = 0
+        v[1] = torch.randint(-3, 4, (K,), generator=g).float() * 2.0 ** -24
+    t = v.to(torch.float16 if dtype == "f16" else torch.bfloat16)
+    return t.float().numpy(), t
+
+
+@pytest.mark.parametrize("M,K,dtype,kind", [(64, 256, "f16", "normal"), (37, 768, "bf16", "huge"),
+                                            (6, 20480, "f16", "nearmax"), (300, 2048, "bf16", "normal"),
+                                            (3, 512, "f16", "zero_tiny"), (4, 1024, "bf16", "nearmax")])
+def test_act_rotate_scaled_bitexact(M, K, dtype, kind):
+    _say(f"range-safe prologue M={M} K={K} {dtype} {kind}")
+    x32, xt = _rs_input(M, K, dtype, kind, seed=M + K)
+    x16g, eg = cr.act_rotate_scaled(xt.to(DEV))
+    x16o, eo = O.rotate_rowscaled_f16(x32)
+    assert np.array_equal(_np(eg).astype(np.int64), eo)
+    assert np.array_equal(_np(x16g).view(np.uint16), x16o.view(np.uint16))
+
+
+def _ulp_out(y, out):
+    a = np.abs(np.asarray(y, np.float64))
+    if out == "f16":
+        return np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - 10)
+    return np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7)
+
+
+@pytest.mark.parametrize("M,N,K,xd,yd,bias,res,kind", [(64, 256, 256, "f16", "f16", False, False, "normal"),
+                                                       (300, 203, 768, "bf16", "bf16", True, True, "normal"),
+                                                       (1024, 2048, 2048, "bf16", "bf16", True, False, "normal"),
+                                                       (37, 80, 512, "f16", "bf16", False, True, "nearmax"),
+                                                       (16, 256, 4096, "f16", "f16", True, True, "normal"),
+                                                       (8, 128, 1024, "bf16", "bf16", False, False, "huge")])
+def test_linear_w8a16_rs_within_tolerance(M, N, K, xd, yd, bias, res, kind):
+    _say(f"range-safe w8a16 M={M} N={N} K={K} {xd}->{yd} bias={bias} residual={res} {kind}")
+    x32, xt = _rs_input(M, K, xd, kind, seed=M + N)
+    qw, sw = O.quantize_weights(wl.make_weights(N, K, seed=M + N).numpy())
+    b = wl.make_bias(N, seed=M) if bias else None
+    ydt = torch.float16 if yd == "f16" else torch.bfloat16
+    r = wl.make_residual(M, N, seed=M).float().to(ydt) if res else None
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    yg = cr.linear_w8a16_rs(xt.to(DEV), t(qw), t(sw), None if b is None else b.to(DEV),
+                            None if r is None else r.to(DEV), out_dtype=ydt)
+    yg = yg.float().cpu().numpy().astype(np.float64)
+    yo = O.linear_w8a16_rs(x32, qw, sw, None if b is None else b.numpy(),
+                           None if r is None else r.float().numpy(), out=yd).astype(np.float64)
+    pre = O.linear_w8a16_rs(x32, qw, sw, None if b is None else b.numpy(), None, out=yd).astype(np.float64)
+    x16s, e = O.rotate_rowscaled_f16(x32)
+    s_main = (np.abs(x16s.astype(np.float64)) @ np.abs(qw.astype(np.float64)).T) * \
+        sw.astype(np.float64)[None, :] * np.exp2(e.astype(np.float64))[:, None]
+    tol = _ulp_out(pre, yd) + (_ulp_out(yo, yd) if res else 0.0) + 2.0 ** -14 * s_main
+    assert np.isfinite(yg).all() and np.isfinite(yo).all()
+    d = np.abs(yg - yo)
+    viol = int((d > tol).sum())
+    rel = float(np.linalg.norm(d) / np.linalg.norm(yo))
+    _say(f"  violations {viol}, max |dY|/tol {float((d / tol).max()):.3f}, rel. Frobenius {rel:.2e}")
+    assert viol == 0 and rel <= 1e-2
