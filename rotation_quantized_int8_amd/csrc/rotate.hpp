@@ -53,18 +53,15 @@ __device__ __forceinline__ double in16_to_f64(uint16_t bits) {
   else return (double)__half2float(__ushort_as_half(bits));
 }
 
-// Steps 1-4 for one group whose row `lane` (elements 16 lane .. 16 lane + 15)
-// this lane already holds as two 16-byte halves r0, r1 of 16-bit values (fp16,
-// or bf16 with kBF16).  On return y[] holds 16 * x_rot of the same row of the
-// group: exact for fp16 inputs, and for bf16 inputs whenever the group's
-// values span at most 45 binades (every partial sum then fits 53 bits).
-// `slot` is the segment's private LDS slot (kSlotBytes); it is free again on
-// return.
+// Steps 2-4 for a group of 16-bit values (fp16, or bf16 with kBF16) already
+// staged in `slot` (row a of the 16x16 view, 32 bytes, at byte 32 a; written
+// by lanes of this wavefront).  On return y[] holds 16 * x_rot of row `lane`
+// of the group: exact for fp16 inputs, and for bf16 inputs whenever the
+// group's values span at most 45 binades (every partial sum then fits 53
+// bits).  `slot` is the segment's private LDS slot (kSlotBytes); it is free
+// again on return.
 template <bool kBF16 = false>
-__device__ __forceinline__ void rotate_loaded(v4i r0, v4i r1, char* slot, int lane, double (&y)[16]) {
-  v4i* st = reinterpret_cast<v4i*>(slot + 32 * lane);
-  st[0] = r0;
-  st[1] = r1;
+__device__ __forceinline__ void rotate_staged(char* slot, int lane, double (&y)[16]) {
   wave_lds_sync();
   // column `lane`: element (a, lane) for a = 0..15
   const uint16_t* sh = reinterpret_cast<const uint16_t*>(slot);
@@ -87,6 +84,16 @@ __device__ __forceinline__ void rotate_loaded(v4i r0, v4i r1, char* slot, int la
   }
   wave_lds_sync();  // reads done before the slot's next use
   fwht16(y);        // along b
+}
+
+// Steps 1-4: this lane holds row `lane` (elements 16 lane .. 16 lane + 15)
+// of the group as two 16-byte halves r0, r1 and parks it in the slot first.
+template <bool kBF16 = false>
+__device__ __forceinline__ void rotate_loaded(v4i r0, v4i r1, char* slot, int lane, double (&y)[16]) {
+  v4i* st = reinterpret_cast<v4i*>(slot + 32 * lane);
+  st[0] = r0;
+  st[1] = r1;
+  rotate_staged<kBF16>(slot, lane, y);
 }
 
 // Loads row `lane` of the group at `src` and rotates it (see rotate_loaded).
