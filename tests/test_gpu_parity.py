@@ -688,3 +688,63 @@ def test_linear_w8a16_rs_within_tolerance(M, N, K, xd, yd, bias, res, kind):
     rel = float(np.linalg.norm(d) / np.linalg.norm(yo))
     _say(f"  violations {viol}, max |dY|/tol {float((d / tol).max()):.3f}, rel. Frobenius {rel:.2e}")
     assert viol == 0 and rel <= 1e-2
+
+
+def test_graph_replays_of_every_path_match_eager():
+    # every entry point captured once in a HIP graph (with its workspace) and
+    # replayed with eager calls in between: each replay equals the eager bits
+    _say("graph replays: fused few-row, LoRA, residual, range-safe, dequantise-every-call")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    K, N = 2048, 2048
+    qw, sw = O.quantize_weights(wl.make_weights(N, K, seed=51).numpy())
+    qw, sw = t(qw), t(sw)
+    d, u = wl.make_lora(N, K, seed=51)
+    lora = (d.to(DEV), u.to(DEV), 0.5)
+    b = wl.make_bias(N, seed=51).to(DEV)
+    xs = {M: wl.make_activations(M, K, seed=M).to(DEV) for M in (1, 16, 300)}
+    res = wl.make_residual(300, N, seed=51).to(DEV)
+    xb = xs[300].to(torch.bfloat16)
+    wss = {
+        "fused": torch.empty(cr.workspace_bytes(cr.PATH_W8A8, 1, N, K), dtype=torch.uint8, device=DEV),
+        "lora16": torch.empty(cr.workspace_bytes(cr.PATH_W8A8, 16, N, K, 32), dtype=torch.uint8, device=DEV),
+        "lora300": torch.empty(cr.workspace_bytes(cr.PATH_W8A8, 300, N, K, 32), dtype=torch.uint8, device=DEV),
+        "rs": torch.empty(cr.workspace_bytes(cr.PATH_W8A16_RS, 300, N, K), dtype=torch.uint8, device=DEV),
+        "dq": torch.empty(cr.workspace_bytes(cr.PATH_DEQUANT, 300, N, K), dtype=torch.uint8, device=DEV),
+    }
+    outs = {
+        "fused": torch.empty((1, N), dtype=torch.float16, device=DEV),
+        "lora16": torch.empty((16, N), dtype=torch.float16, device=DEV),
+        "lora300": torch.empty((300, N), dtype=torch.float16, device=DEV),
+        "rs": torch.empty((300, N), dtype=torch.bfloat16, device=DEV),
+    }
+
+    def calls():
+        cr.linear_w8a8_ex(xs[1], qw, sw, bias=b, out=outs["fused"], workspace=wss["fused"])
+        cr.linear_w8a8_ex(xs[16], qw, sw, bias=b, lora=lora, out=outs["lora16"], workspace=wss["lora16"])
+        cr.linear_w8a8_ex(xs[300], qw, sw, bias=b, lora=lora, residual=res, out=outs["lora300"],
+                          workspace=wss["lora300"])
+        cr.linear_w8a16_rs(xb, qw, sw, bias=b, out=outs["rs"], workspace=wss["rs"])
+        return cr.linear_dequant(xs[300], qw, sw, b, workspace=wss["dq"])
+
+    ref_dq = calls().clone()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in outs.items()}
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            dq = calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()
+        dq.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v.view(torch.int16), ref[k].view(torch.int16)), f"{k}, replay {rep}"
+        assert torch.equal(dq.view(torch.int16), ref_dq.view(torch.int16)), f"dequant, replay {rep}"
+        calls()                       # eager work between replays
+        torch.cuda.synchronize()
+    _say("  3 replays of 5 entry points equal to eager")
