@@ -58,6 +58,11 @@ Readings where the pages leave a step open:
       residual is one addition in that type.  The fp32 accumulation of the
       MFMA path has no K limit (the pages' fp16 accumulation needs fp32 for
       K > 65504).
+  R12 an empty contraction ([P4], the commit that returns empty contractions
+      early): with K = 0 every sum over k is empty, so A = 0, a row maximum is
+      0 (a zero row in R4's sense: s = 0, e = 0) and the LoRA term is 0; each
+      path's formula then gives Y = out(+0 + bias), or +0 without a bias, with
+      a residual added as usual.  K = 0 is therefore a valid size.
 """
 
 from __future__ import annotations
@@ -150,8 +155,8 @@ def hadamard256() -> np.ndarray:
 
 
 def _check_k(K: int) -> None:
-    if K % GROUP != 0 or K <= 0 or K > K_MAX:
-        raise ValueError(f"K={K} must be a positive multiple of {GROUP} and <= {K_MAX}")
+    if K % GROUP != 0 or K < 0 or K > K_MAX:
+        raise ValueError(f"K={K} must be a multiple of {GROUP} in 0 .. {K_MAX} (R7, R12)")
 
 
 # ---------------------------------------------------------------------------
@@ -237,7 +242,7 @@ def quantize_rows(v32: np.ndarray):
     row gets s = 0 and Q = 0 (R4).  Returns (Q int8 [R, K], s fp32 [R]).
     """
     v = np.asarray(v32, dtype=np.float32)
-    amax = np.max(np.abs(v), axis=1)
+    amax = np.max(np.abs(v), axis=1, initial=np.float32(0))   # an empty row (K = 0) has maximum 0 (R12)
     s = (amax / np.float32(QMAX)).astype(np.float32)
     safe = np.where(s == 0, np.float32(1), s).astype(np.float32)
     r = (v / safe[:, None]).astype(np.float32)
@@ -446,7 +451,7 @@ def rotate_rowscaled_f16(x):
     e = np.zeros(M, np.int64)
     for m in range(M):
         if exact_row[m]:
-            amax = float(np.max(np.abs(xr[m])))
+            amax = float(np.max(np.abs(xr[m]), initial=0.0))   # K = 0: maximum 0, e = 0 (R12)
             if amax > 0:
                 f, ex2 = math.frexp(amax)
                 e[m] = ex2 - 1 if f == 0.5 else ex2

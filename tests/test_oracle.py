@@ -665,3 +665,49 @@ def test_linear_w8a16_rs_near_max_inputs_finite_and_accurate():
     truth = x.astype(np.float64) @ O.dequantize_weights(qw, sw).astype(np.float64).T
     assert np.isfinite(rs).all()
     assert np.linalg.norm(rs - truth) <= 1e-2 * np.linalg.norm(truth)
+
+
+# ------------------------------------------------- empty contraction (R12)
+
+def test_empty_contraction_equals_zero_activation_rows():
+    # With K = 0 every sum over k is empty, so each path must give exactly
+    # what an all-zero activation row gives at any K (where the sums are sums
+    # of zeros): pinned against the K = 256 computation through the general
+    # formulas, bit for bit, and against the closed form fp16(+0 + bias).
+    rng = np.random.default_rng(12)
+    M, N, R = 3, 6, 4
+    bias = np.array([0.5, -0.0, 1e-9, -3.25, 70000.0, 2.0 ** -20], np.float32)
+    res16 = rng.normal(size=(M, N)).astype(np.float16)
+    res32 = O.to_bf16(rng.normal(size=(M, N)))
+    up = rng.normal(size=(N, R)).astype(np.float32)
+    w = rng.normal(size=(N, 256)).astype(np.float32) * 0.02
+    qw, sw = O.quantize_weights(w)
+    qw0, sw0 = O.quantize_weights(np.zeros((N, 0), np.float32))
+    assert qw0.shape == (N, 0) and np.array_equal(sw0, np.zeros(N, np.float32))
+    x0 = np.zeros((M, 0), np.float16)
+    xz = np.zeros((M, 256), np.float16)
+    lora0 = (np.zeros((R, 0), np.float32), up, 0.5)
+    loraz = (rng.normal(size=(R, 256)).astype(np.float32), up, 0.5)
+
+    def same(a, b):
+        a, b = np.asarray(a), np.asarray(b)
+        assert a.dtype == b.dtype and a.shape == b.shape
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+    same(O.linear_w8a8(x0, qw0, sw0, bias)[0], O.linear_w8a8(xz, qw, sw, bias)[0])
+    same(O.linear_w8a8_ex(x0, qw0, sw0, bias, lora0, res16), O.linear_w8a8_ex(xz, qw, sw, bias, loraz, res16))
+    same(O.linear_w8a16(x0, qw0, sw0, bias, lora0), O.linear_w8a16(xz, qw, sw, bias, loraz))
+    same(O.linear_dequant(x0, qw0, sw0, bias), O.linear_dequant(xz, qw, sw, bias))
+    for out, res in (("f16", res16), ("bf16", res32)):
+        same(O.linear_w8a16_rs(x0, qw0, sw0, bias, res, out=out), O.linear_w8a16_rs(xz, qw, sw, bias, res, out=out))
+    closed = np.broadcast_to((np.float32(0) + bias).astype(np.float16), (M, N))
+    same(O.linear_w8a8(x0, qw0, sw0, bias)[0], np.ascontiguousarray(closed))
+    assert not np.signbit(O.linear_w8a8(x0, qw0, sw0, bias)[0][:, 1]).any()   # -0 bias gives +0
+    same(O.linear_f16(x0, np.zeros((N, 0), np.float16)), np.zeros((M, N), np.float16))
+    q0, s0 = O.quantize_activations(x0)
+    assert q0.shape == (M, 0) and np.array_equal(s0, np.zeros(M, np.float32))
+    x16, e = O.rotate_rowscaled_f16(x0)
+    assert x16.shape == (M, 0) and np.array_equal(e, np.zeros(M, np.int64))
+    assert O.int8_gemm(np.zeros((M, 0), np.int8), qw0).shape == (M, N)
+    with pytest.raises(ValueError):
+        O.quantize_weights(np.zeros((N, 128), np.float32))
