@@ -34,9 +34,16 @@
  *     and the call returns without synchronising.  All argument checks run on
  *     the host before anything is enqueued; on an error nothing is enqueued
  *     and no output is touched.
- *   - Sizes are int64_t.  K must be a positive multiple of 256 and at most
- *     131072 (so 127 * 127 * K < 2^31 and the int32 accumulator cannot
- *     overflow).  M == 0 or N == 0 is a valid empty call: nothing is launched.
+ *   - Sizes are int64_t.  K must be a multiple of 256 and at most 131072
+ *     (so 127 * 127 * K < 2^31 and the int32 accumulator cannot overflow).
+ *     M == 0 or N == 0 is a valid empty call: nothing is launched.
+ *   - K == 0 is an empty contraction (page "[PR #249] Add an mps backend
+ *     ...", commit list: empty contractions return early): every sum over k
+ *     is empty, so A = 0, a row maximum is 0 (s_X, s_W and the range-safe
+ *     exponent are 0, as for a zero row), a LoRA term is 0, and a linear
+ *     writes Y = out(+0 + bias[n]) (+0 without a bias) plus its residual as
+ *     usual.  Arrays with no elements (X, Q_X, Q_W, W16, X16, lora.down) are
+ *     not touched and may be NULL; no workspace is needed.
  *   - Outputs must not overlap inputs or the workspace (one exception: the
  *     residual of convrot_linear_w8a8_ex may be its output buffer).
  *   - Errors are returned as status codes; nothing is printed, thrown or
@@ -109,7 +116,8 @@ convrot_status convrot_quantize_weights(const float* W, int64_t N, int64_t K,
  * (path = CONVROT_PATH_W8A8), convrot_linear_w8a16 (path =
  * CONVROT_PATH_W8A16) or convrot_linear_dequant (path =
  * CONVROT_PATH_DEQUANT, lora_rank 0) need for these sizes, with lora_rank = 0
- * without LoRA; 0 for an empty problem, (size_t)-1 for invalid sizes. */
+ * without LoRA; 0 for an empty problem (M, N or K zero), (size_t)-1 for
+ * invalid sizes. */
 size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_t lora_rank);
 
 /* The W8A8 ConvRot linear ("What changed in the computation", activation
@@ -225,7 +233,7 @@ convrot_status convrot_gemm_i8_f16(const int8_t* Q_X, const float* s_X,
 
 /* fp16 baseline GEMM (the fp16 column of the six-shape table of [P1]):
  * Y fp16 [M, N] = X fp16 [M, K] . W fp16 [N, K]^T, fp32 accumulation.
- * K must be a positive multiple of 256 here as well. */
+ * K must be a multiple of 256 here as well (K == 0 gives Y = +0). */
 convrot_status convrot_gemm_f16(const void* X, const void* W,
                                 int64_t M, int64_t N, int64_t K, void* Y, void* stream);
 

@@ -157,7 +157,10 @@ def _flatten(x: torch.Tensor):
     if x.dim() == 0:
         raise ValueError("input must have at least one dimension")
     lead = x.shape[:-1]
-    return x.reshape(-1, x.shape[-1]), lead
+    rows = 1
+    for d in lead:
+        rows *= d
+    return x.reshape(rows, x.shape[-1]), lead   # explicit rows: K may be 0
 
 
 def linear_w8a8(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,

@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <initializer_list>
 
 #include "convrot.h"
 #include "launch.hpp"
@@ -35,7 +36,9 @@ convrot_status check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool k_ok(int64_t K) { return K > 0 && K % kGroup == 0 && K <= kKMax; }
+// K = 0 is an empty contraction (see empty_linear); otherwise a multiple of
+// the group size up to kKMax.
+bool k_ok(int64_t K) { return K >= 0 && K % kGroup == 0 && K <= kKMax; }
 
 // [a, a + na) and [b, b + nb) overlap?  (null or empty ranges never overlap)
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -80,6 +83,47 @@ convrot_status launched(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CO
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+struct In {
+  const void* p;
+  size_t bytes;
+};
+
+// A linear with K = 0 (an empty contraction): every sum over k is empty, so
+// Y = out(+0 + bias) (+0 without a bias) plus the residual (which may be Y
+// itself); an int32 output is all zero.  `required` are the inputs with
+// elements (scales), which must be present, aligned and apart from Y; the
+// arrays with no elements (X, Q_X, Q_W, lora.down) are not touched and may
+// be null.  No workspace is used.
+convrot_status empty_linear(int64_t M, int64_t N, std::initializer_list<In> required, const float* bias,
+                            const convrot_lora* lora, const void* residual, void* Y, EmptyOut out,
+                            void* stream) {
+  if (!Y || (lora && !lora->up)) return CONVROT_ERR_INVALID_ARG;
+  for (const In& r : required)
+    if (!r.p) return CONVROT_ERR_INVALID_ARG;
+  bool aligned = aligned16(Y) && (!bias || aligned16(bias)) && (!residual || aligned16(residual)) &&
+                 (!lora || (aligned16(lora->up) && (!lora->down || aligned16(lora->down))));
+  for (const In& r : required) aligned = aligned && aligned16(r.p);
+  if (!aligned) return CONVROT_ERR_ALIGNMENT;
+  const size_t yb = (size_t)M * N * (out == kEmptyI32 ? 4 : 2);
+  if (overlap(Y, yb, bias, bias ? (size_t)N * 4 : 0) ||
+      (residual != Y && overlap(Y, yb, residual, residual ? yb : 0)) ||
+      (lora && overlap(Y, yb, lora->up, (size_t)N * lora->rank * 4)))
+    return CONVROT_ERR_INVALID_ARG;
+  for (const In& r : required)
+    if (overlap(Y, yb, r.p, r.bytes)) return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  return launched(launch_empty_linear(M, N, bias, residual, out, Y, as_stream(stream)));
+}
+
+// K = 0 for a per-row output (a scale or an exponent): the row maximum over
+// no elements is 0.
+convrot_status empty_rows(void* v, int64_t rows, void* stream) {
+  if (!v) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(v)) return CONVROT_ERR_ALIGNMENT;
+  if (convrot_status st = check_device()) return st;
+  return launched(launch_fill32(v, rows, 0u, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,7 +134,7 @@ const char* convrot_status_string(int status) {
   switch (status) {
     case CONVROT_OK: return "ok";
     case CONVROT_ERR_INVALID_ARG: return "invalid argument (null pointer or overlapping output)";
-    case CONVROT_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 256 in 256..131072, or bad LoRA rank)";
+    case CONVROT_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 256 in 0..131072, or bad LoRA rank)";
     case CONVROT_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
     case CONVROT_ERR_DEVICE: return "current HIP device is not gfx950 or cannot be queried";
     case CONVROT_ERR_LAUNCH: return "kernel launch failed";
@@ -103,6 +147,11 @@ size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_
   if (M < 0 || N < 0 || K < 0 || lora_rank < 0 || lora_rank > CONVROT_LORA_RANK_MAX) return (size_t)-1;
   if (M == 0 || N == 0) return 0;
   if (!k_ok(K)) return (size_t)-1;
+  if (K == 0) {   // an empty contraction needs no workspace
+    if (path == CONVROT_PATH_W8A8 || path == CONVROT_PATH_W8A16) return 0;
+    if (path == CONVROT_PATH_DEQUANT || path == CONVROT_PATH_W8A16_RS) return lora_rank == 0 ? 0 : (size_t)-1;
+    return (size_t)-1;
+  }
   if (path == CONVROT_PATH_W8A8) {
     const W8A8Plan plan = w8a8_plan(M, N, K, lora_rank > 0);
     return round256((size_t)M * K) + round256((size_t)M * 4) +
@@ -120,6 +169,7 @@ convrot_status convrot_quantize_weights(const float* W, int64_t N, int64_t K, in
   if (N < 0 || K < 0) return CONVROT_ERR_SHAPE;
   if (N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return empty_rows(s_W, N, stream);   // s_W = 0, Q_W has no elements
   if (!W || !Q_W || !s_W) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(W) || !aligned16(Q_W) || !aligned16(s_W)) return CONVROT_ERR_ALIGNMENT;
   const size_t wb = (size_t)N * K * 4, qb = (size_t)N * K, sb = (size_t)N * 4;
@@ -134,6 +184,7 @@ convrot_status convrot_act_quant(const void* X, int64_t M, int64_t K, int8_t* Q_
   if (M < 0 || K < 0) return CONVROT_ERR_SHAPE;
   if (M == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return empty_rows(s_X, M, stream);   // s_X = 0, Q_X has no elements
   if (!X || !Q_X || !s_X) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(Q_X) || !aligned16(s_X)) return CONVROT_ERR_ALIGNMENT;
   const size_t xb = (size_t)M * K * 2, qb = (size_t)M * K, sb = (size_t)M * 4;
@@ -148,6 +199,7 @@ convrot_status convrot_act_rotate_f16(const void* X, int64_t M, int64_t K, void*
   if (M < 0 || K < 0) return CONVROT_ERR_SHAPE;
   if (M == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return check_device();               // X16 has no elements
   if (!X || !X16) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(X16)) return CONVROT_ERR_ALIGNMENT;
   if (overlap(X16, (size_t)M * K * 2, X, (size_t)M * K * 2)) return CONVROT_ERR_INVALID_ARG;
@@ -160,6 +212,7 @@ convrot_status convrot_gemm_i8_i32(const int8_t* Q_X, const int8_t* Q_W, int64_t
   if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return empty_linear(M, N, {}, nullptr, nullptr, nullptr, A, kEmptyI32, stream);
   if (!Q_X || !Q_W || !A) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(Q_X) || !aligned16(Q_W) || !aligned16(A)) return CONVROT_ERR_ALIGNMENT;
   const size_t ab = (size_t)M * N * 4;
@@ -192,6 +245,9 @@ convrot_status convrot_gemm_i8_f16(const int8_t* Q_X, const float* s_X, const in
   if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0)
+    return empty_linear(M, N, {{s_X, (size_t)M * 4}, {s_W, (size_t)N * 4}}, bias, nullptr, nullptr, Y, kEmptyF16,
+                        stream);
   if (convrot_status st = check_gemm_i8_f16(Q_X, s_X, Q_W, s_W, bias, M, N, K, Y)) return st;
   if (convrot_status st = check_device()) return st;
   GemmArgs g{};
@@ -205,6 +261,7 @@ convrot_status convrot_gemm_f16(const void* X, const void* W, int64_t M, int64_t
   if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return empty_linear(M, N, {}, nullptr, nullptr, nullptr, Y, kEmptyF16, stream);
   if (!X || !W || !Y) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return CONVROT_ERR_ALIGNMENT;
   const size_t yb = (size_t)M * N * 2;
@@ -233,6 +290,7 @@ convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_
   if (lora && (rank < 1 || rank > CONVROT_LORA_RANK_MAX)) return CONVROT_ERR_SHAPE;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return empty_linear(M, N, {{s_W, (size_t)N * 4}}, bias, lora, residual, Y, kEmptyF16, stream);
   if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
   if (lora && (!lora->down || !lora->up)) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
@@ -328,6 +386,7 @@ convrot_status convrot_dequantize_weights(const int8_t* Q_W, const float* s_W, i
   if (N < 0 || K < 0) return CONVROT_ERR_SHAPE;
   if (N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return check_device();               // W16 has no elements
   if (!Q_W || !s_W || !W16) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(Q_W) || !aligned16(s_W) || !aligned16(W16)) return CONVROT_ERR_ALIGNMENT;
   const size_t wb = (size_t)N * K * 2;
@@ -343,6 +402,7 @@ convrot_status convrot_linear_dequant(const void* X, int64_t M, int64_t K, const
   if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return empty_linear(M, N, {{s_W, (size_t)N * 4}}, bias, nullptr, nullptr, Y, kEmptyF16, stream);
   if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
       (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
@@ -370,6 +430,7 @@ convrot_status convrot_act_rotate_scaled(const void* X, int x_dtype, int64_t M, 
   if (x_dtype != CONVROT_DTYPE_F16 && x_dtype != CONVROT_DTYPE_BF16) return CONVROT_ERR_INVALID_ARG;
   if (M == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return empty_rows(rowexp, M, stream);   // e = 0, X16 has no elements
   if (!X || !X16 || !rowexp) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(X16) || !aligned16(rowexp)) return CONVROT_ERR_ALIGNMENT;
   const size_t xb = (size_t)M * K * 2, eb = (size_t)M * 4;
@@ -389,6 +450,9 @@ convrot_status convrot_linear_w8a16_rs(const void* X, int x_dtype, int64_t M, in
     return CONVROT_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0)
+    return empty_linear(M, N, {{s_W, (size_t)N * 4}}, bias, nullptr, residual, Y,
+                        y_dtype == CONVROT_DTYPE_BF16 ? kEmptyBF16 : kEmptyF16, stream);
   if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||
       (bias && !aligned16(bias)) || (residual && !aligned16(residual)) || (workspace && !aligned16(workspace)))
@@ -427,6 +491,7 @@ convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const i
   if (lora && (rank < 1 || rank > CONVROT_LORA_RANK_MAX)) return CONVROT_ERR_SHAPE;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0) return empty_linear(M, N, {{s_W, (size_t)N * 4}}, bias, lora, nullptr, Y, kEmptyF16, stream);
   if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
   if (lora && (!lora->down || !lora->up)) return CONVROT_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) ||

@@ -38,6 +38,15 @@ __device__ __forceinline__ __half f64_to_f16_rn(double d) {
   return __float2half_rn(f);
 }
 
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN), and back.
+__device__ __forceinline__ uint16_t f32_to_bf16_rn(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
 // One DPP lane permutation of a float inside each 16-lane row of the wave.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {

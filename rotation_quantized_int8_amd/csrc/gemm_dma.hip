@@ -121,15 +121,6 @@ __device__ __forceinline__ v8h lora_frag(const __half* __restrict__ base, int64_
   return *reinterpret_cast<const v8h*>(&v);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN), and back.
-__device__ __forceinline__ uint16_t f32_to_bf16_rn(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
 // Eight bf16 additions, each rounded once: a + b in fp32 (fp32 carries more
 // than twice bf16's precision, so this is the correctly rounded bf16 sum).
 __device__ __forceinline__ v4i add_bf16x8(v4i a, v4i b) {

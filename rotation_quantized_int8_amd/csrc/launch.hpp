@@ -84,4 +84,12 @@ hipError_t launch_lora_prep(const void* X, const float* down, const float* up, f
                             int64_t N, int64_t K, int rank, int t_ld, float* P, __half* T, __half* U,
                             hipStream_t stream);
 
+// Empty contractions (K = 0).  Y [M, N] = +0 + bias[n] (or +0) rounded to
+// the output type, then the residual R (same type, may be Y) added once;
+// int32 output: all zero.  fill32 writes n copies of a 32-bit word.
+enum EmptyOut { kEmptyF16 = 0, kEmptyBF16 = 1, kEmptyI32 = 2 };
+hipError_t launch_empty_linear(int64_t M, int64_t N, const float* bias, const void* R, EmptyOut out, void* Y,
+                               hipStream_t stream);
+hipError_t launch_fill32(void* p, int64_t n, uint32_t value, hipStream_t stream);
+
 }  // namespace convrot

@@ -68,6 +68,14 @@ def test_workspace_bytes(L):
     # range-safe weight-only: fp16 activation [M, K] and the row exponents [M]
     assert L.convrot_workspace_bytes(3, 4, 8, 256, 0) == 2048 + 256
     assert L.convrot_workspace_bytes(3, 4, 8, 256, 1) == bad
+    # K = 0 (an empty contraction) needs no workspace on any path
+    for path in (0, 1, 2, 3):
+        assert L.convrot_workspace_bytes(path, 4, 8, 0, 0) == 0
+    assert L.convrot_workspace_bytes(0, 4, 8, 0, 32) == 0
+    assert L.convrot_workspace_bytes(1, 4, 8, 0, 32) == 0
+    assert L.convrot_workspace_bytes(2, 4, 8, 0, 1) == bad
+    assert L.convrot_workspace_bytes(3, 4, 8, 0, 1) == bad
+    assert L.convrot_workspace_bytes(0, 4, 8, -256, 0) == bad
 
 
 P = 1 << 20          # a fake, 16-byte aligned "device" address: never dereferenced
@@ -84,7 +92,6 @@ def test_linear_w8a8_argument_errors(L):
     assert f(None, 4, 256, None, None, 0, None, None, None, 0, None) == OK
     # shapes
     assert f(P, 4, 255, Q, R, 8, None, S, S + 4096, ws, None) == SHAPE
-    assert f(P, 4, 0, Q, R, 8, None, S, S + 4096, ws, None) == SHAPE
     assert f(P, -1, 256, Q, R, 8, None, S, S + 4096, ws, None) == SHAPE
     assert f(P, 4, 131072 + 256, Q, R, 8, None, S, S + 4096, ws, None) == SHAPE
     # null pointers
@@ -198,6 +205,43 @@ def test_stage_argument_errors(L):
     assert L.convrot_quantize_weights(P, 8, 256, Q, Q + 16, None) == INVALID
     assert L.convrot_quantize_weights(P, -8, 256, Q, R, None) == SHAPE
     assert L.convrot_quantize_weights(None, 0, 256, None, None, None) == OK
+
+
+def test_empty_contraction_argument_errors(L):
+    # K = 0: X, Q_X, Q_W and lora.down have no elements and may be NULL, but
+    # the scales, the output and the other operands with elements are checked
+    # as usual (every call here fails before the device check)
+    f = L.convrot_linear_w8a8
+    assert f(None, 4, 0, None, None, 8, None, S, None, 0, None) == INVALID       # s_W
+    assert f(None, 4, 0, None, R, 8, None, None, None, 0, None) == INVALID       # Y
+    assert f(None, 4, 0, None, R, 8, None, S + 2, None, 0, None) == ALIGN
+    assert f(None, 4, 0, None, R, 8, R + 4, S, None, 0, None) == ALIGN         # bias
+    assert f(None, 4, 0, None, R, 8, S + 16, S, None, 0, None) == INVALID      # bias inside Y
+    assert f(None, 4, 0, None, S + 32, 8, None, S, None, 0, None) == INVALID   # s_W inside Y
+    fx = L.convrot_linear_w8a8_ex
+    Y = S
+    lora = cr._Lora(None, None, 4, 1.0)
+    assert fx(None, 4, 0, None, R, 8, None, ctypes.byref(lora), None, Y, None, 0, None) == INVALID  # up
+    lora = cr._Lora(None, Q, 0, 1.0)
+    assert fx(None, 4, 0, None, R, 8, None, ctypes.byref(lora), None, Y, None, 0, None) == SHAPE
+    lora = cr._Lora(None, Y + 16, 4, 1.0)
+    assert fx(None, 4, 0, None, R, 8, None, ctypes.byref(lora), None, Y, None, 0, None) == INVALID
+    assert fx(None, 4, 0, None, R, 8, None, None, Y + 2, Y, None, 0, None) == ALIGN   # residual
+    assert fx(None, 4, 0, None, R, 8, None, None, Y + 16, Y, None, 0, None) == INVALID
+    assert L.convrot_linear_w8a16(None, 4, 0, None, None, 8, None, None, Y, None, 0, None) == INVALID
+    assert L.convrot_linear_dequant(None, 4, 0, None, R, 8, None, None, None, 0, None) == INVALID
+    assert L.convrot_linear_w8a16_rs(None, 0, 4, 0, None, R, 8, None, None, None, 1, None, 0, None) == INVALID
+    assert L.convrot_linear_w8a16_rs(None, 2, 4, 0, None, R, 8, None, None, Y, 1, None, 0, None) == INVALID
+    assert L.convrot_quantize_weights(None, 8, 0, None, None, None) == INVALID  # s_W
+    assert L.convrot_quantize_weights(None, 8, 0, None, R + 4, None) == ALIGN
+    assert L.convrot_act_quant(None, 4, 0, None, None, None) == INVALID          # s_X
+    assert L.convrot_act_rotate_scaled(None, 0, 4, 0, None, None, None) == INVALID  # e
+    assert L.convrot_gemm_i8_i32(None, None, 4, 8, 0, None, None) == INVALID     # A
+    assert L.convrot_gemm_i8_f16(None, None, None, R, None, 4, 8, 0, S, None) == INVALID   # s_X
+    assert L.convrot_gemm_i8_f16(None, P, None, None, None, 4, 8, 0, S, None) == INVALID   # s_W
+    assert L.convrot_gemm_f16(None, None, 4, 8, 0, None, None) == INVALID        # Y
+    assert L.convrot_gemm_f16(None, None, 4, 8, 0, S + 8, None) == ALIGN
+    assert L.convrot_quantize_weights(None, 8, -256, None, R, None) == SHAPE
 
 
 def test_python_wrapper_refuses_cpu_tensors():

@@ -748,3 +748,73 @@ def test_graph_replays_of_every_path_match_eager():
         calls()                       # eager work between replays
         torch.cuda.synchronize()
     _say("  3 replays of 5 entry points equal to eager")
+
+
+def test_empty_contraction_every_entry_point():
+    # K = 0: every sum over k is empty (the oracle's reading of empty
+    # contractions); outputs are pre-filled with NaN so that every element
+    # must be written
+    _say("K = 0 (empty contraction) on every entry point")
+    M, N, R = 5, 24, 4
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    g = np.random.default_rng(0)
+    bias_np = g.normal(size=N).astype(np.float32)
+    bias_np[1] = -0.0
+    bias_np[2] = 7e4     # rounds to fp16 inf
+    bias = t(bias_np)
+    res_np = g.normal(size=(M, N)).astype(np.float16)
+    up_np = g.normal(size=(N, R)).astype(np.float32)
+    x0 = torch.empty((M, 0), dtype=torch.float16, device=DEV)
+    qw0, sw0 = cr.quantize_weights(torch.empty((N, 0), dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert qw0.shape == (N, 0) and torch.equal(sw0.cpu(), torch.zeros(N))
+    sw = t(g.random(N).astype(np.float32) * 0.01)   # any scale: K = 0 does not read it
+    down0 = torch.empty((R, 0), dtype=torch.float32, device=DEV)
+    lora = (down0, t(up_np), 0.5)
+    x0n = np.zeros((M, 0), np.float16)
+    qw0n = np.zeros((N, 0), np.int8)
+    lora_n = (np.zeros((R, 0), np.float32), up_np, 0.5)
+
+    def bits(a):
+        a = np.asarray(a)
+        return a.view(np.uint16) if a.dtype in (np.float16,) else a.view(np.uint8)
+
+    def nan_out(dtype):
+        return torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
+
+    y = cr.linear_w8a8(x0, qw0, sw, bias)
+    exp = O.linear_w8a8(x0n, qw0n, sw.cpu().numpy(), bias_np)[0]
+    assert np.array_equal(bits(_np(y)), bits(exp))
+    y = cr.linear_w8a8_ex(x0, qw0, sw, bias=bias, lora=lora, residual=t(res_np), out=nan_out(torch.float16))
+    exp = O.linear_w8a8_ex(x0n, qw0n, sw.cpu().numpy(), bias_np, lora_n, res_np)
+    assert np.array_equal(bits(_np(y)), bits(exp))
+    r = t(res_np)
+    cr.linear_w8a8_ex(x0, qw0, sw, bias=bias, residual=r, out=r)       # in place
+    assert np.array_equal(bits(_np(r)), bits(O.linear_w8a8_ex(x0n, qw0n, sw.cpu().numpy(), bias_np, None, res_np)))
+    y = cr.linear_w8a16(x0, qw0, sw, bias, lora=lora)
+    exp = O.linear_w8a16(x0n, qw0n, sw.cpu().numpy(), bias_np, lora_n)
+    assert np.array_equal(bits(_np(y)), bits(exp))
+    y = cr.linear_dequant(x0, qw0, sw, bias)
+    assert np.array_equal(bits(_np(y)), bits(O.linear_dequant(x0n, qw0n, sw.cpu().numpy(), bias_np)))
+    for dt, name in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
+        res_t = t(res_np).to(dt)
+        res_ref = res_t.float().cpu().numpy()
+        y = cr.linear_w8a16_rs(x0.to(dt), qw0, sw, bias, residual=res_t, out=torch.full((M, N), float("nan"),
+                               dtype=dt, device=DEV))
+        exp = O.linear_w8a16_rs(x0n, qw0n, sw.cpu().numpy(), bias_np, res_ref, out=name)
+        assert np.array_equal(y.float().cpu().numpy().view(np.uint32), np.asarray(exp, np.float32).view(np.uint32)), name
+    q, s = cr.act_quant(x0)
+    assert q.shape == (M, 0) and torch.equal(s.cpu(), torch.zeros(M))
+    assert cr.act_rotate_f16(x0).shape == (M, 0)
+    x16, e = cr.act_rotate_scaled(x0)
+    assert x16.shape == (M, 0) and torch.equal(e.cpu(), torch.zeros(M, dtype=torch.int32))
+    a = cr.gemm_i8_i32(q, qw0)
+    assert torch.equal(a.cpu(), torch.zeros((M, N), dtype=torch.int32))
+    y = cr.gemm_i8_f16(q, s, qw0, sw, bias)
+    assert np.array_equal(bits(_np(y)), bits(O.epilogue_w8a8(np.zeros((M, N), np.int64), np.zeros(M, np.float32),
+                                                             sw.cpu().numpy(), bias_np)))
+    y = cr.gemm_f16(x0, torch.empty((N, 0), dtype=torch.float16, device=DEV))
+    assert torch.equal(y.cpu().view(torch.int16), torch.zeros((M, N), dtype=torch.int16))
+    assert cr.dequantize_weights(qw0, sw).shape == (N, 0)
+    torch.cuda.synchronize()
+    _say("  every entry point bit-exact at K = 0")
