@@ -162,10 +162,88 @@ def summarize_pmc(fetch_csv, write_csv):
         "copy_calibration": {"bytes": COPY_BYTES, "fetch_factor": round(fr, 4), "write_factor": round(wr, 4)},
         "hbm_bytes_per_launch": round(per_launch),
     }
+    # the activation prologue of the same run (not the roofline kernel)
+    pf = [v for (k, v) in fetch if "prologue_kernel" in k]
+    pw = [v for (k, v) in write if "prologue_kernel" in k]
+    if pf and len(pf) == len(pw):
+        import workload as wl
+        layers = sum(n for (_, _, n) in wl.LAYER_SHAPES)
+        algo = sum((3.0 * wl.M_FIXED * k + 4.0 * wl.M_FIXED) * n for (_, k, n) in wl.LAYER_SHAPES) / layers
+        rec["prologue"] = {
+            "kernel": "prologue_kernel",
+            "launches": len(pf),
+            "fetch_kib_per_launch_raw": round(sum(pf) / len(pf), 1),
+            "write_kib_per_launch_raw": round(sum(pw) / len(pw), 1),
+            "hbm_bytes_per_launch": round((sum(pf) * fr + sum(pw) * wr) * 1024.0 / len(pf)),
+            "algorithmic_bytes_per_launch": round(algo),
+        }
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+
+
+def device_peak_int8_tops(dev_index):
+    """Dense int8 MFMA peak re-derived from the device: compute units x peak
+    engine clock x 8192 int8 operations per CU per clock (four SIMDs, one
+    16x16x64 int8 MFMA of 32768 operations per 16 clocks each)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    clock_khz, cus = ctypes.c_int(0), ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(clock_khz), 5, dev_index) != 0:   # hipDeviceAttributeClockRate
+        return None
+    if hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, dev_index) != 0:        # ...MultiprocessorCount
+        return None
+    return {"compute_units": cus.value, "peak_clock_mhz": clock_khz.value / 1e3,
+            "int8_tops": round(cus.value * clock_khz.value * 1e3 * 8192 / 1e12, 1)}
+
+
+def device_copy_gbs(torch, dev, stream):
+    """Device-to-device copy rate (bytes read + bytes written per second) of
+    1 GiB, beyond the memory-side cache: the practical HBM ceiling."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    best = None
+    with torch.cuda.stream(stream):
+        for _ in range(6):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            b.copy_(a)
+            t1.record(stream)
+            t1.synchronize()
+            ms = t0.elapsed_time(t1)
+            best = ms if best is None else min(best, ms)
+    del a, b
+    return round(2.0 * n / (best * 1e-3) / 1e9, 1)
+
+
+def prologue_at_hbm_scale(L, torch, wl, dev, stream):
+    """The activation prologue alone at M = 16384, K = 8192: two 256 MiB fp16
+    inputs used in turn (with the 128 MiB int8 output, beyond the 256 MB
+    memory-side cache), 10 calls per graph; algorithmic bytes 3 M K + 4 M."""
+    M, K = 16384, 8192
+    xs = [wl.make_activations(M, K, seed=i).to(dev) for i in range(2)]
+    qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sx = torch.empty(M, dtype=torch.float32, device=dev)
+
+    def run():
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(10):
+            st = L.convrot_act_quant(xs[i % 2].data_ptr(), M, K, qx.data_ptr(), sx.data_ptr(), h)
+            if st:
+                raise RuntimeError(L.convrot_status_string(st).decode())
+
+    with torch.cuda.stream(stream):
+        g = capture(run, stream)
+        ms = timed_graph(g, 5, 2, stream) / 10
+        del g
+    del xs, qx, sx
+    torch.cuda.empty_cache()
+    gbs = (3.0 * M * K + 4.0 * M) / (ms * 1e-3) / 1e9
+    return {"M": M, "K": K, "us_per_call": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+            "frac_of_8tbs": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 M_SWEEP = (1, 16, 128, 1024, 4096, 16384)
@@ -323,7 +401,7 @@ def main():
     f8a8 = L.convrot_linear_w8a8
     fpro = L.convrot_act_quant
     fgemm = L.convrot_gemm_i8_f16
-    for s in per_shape:   # Q_X / s_X for the GEMM-only legs
+    for s in (per_shape if not args.profile_kernels else []):   # Q_X / s_X for the GEMM-only legs
         st = fpro(s["x"].data_ptr(), M, s["K"], s["qx"].data_ptr(), s["sx"].data_ptr(),
                   torch.cuda.current_stream().cuda_stream)
         if st:
@@ -495,12 +573,19 @@ def main():
                 compare[name] = {"ms_per_step": round(t, 4),
                                  "tops": round(ops_step / (t * 1e-3) / 1e12, 1)}
 
+        log("prologue at HBM scale (M = 16384, K = 8192) and the device copy rate")
+        pro_large = prologue_at_hbm_scale(L, torch, wl, dev, stream)
+        copy_gbs = device_copy_gbs(torch, dev, stream)
+        pro_large["frac_of_device_copy"] = round(pro_large["gbs"] / copy_gbs, 4)
+
         msweep = None
         if not args.no_m_sweep:
             log("row-count sweep on 8192x2048 and 2048x8192")
             msweep = m_sweep(cr, L, stream, dev)
 
     n_launch = sum(s["layers"] for s in per_shape)
+    pro_bytes = sum((3.0 * M * s["K"] + 4.0 * M) * s["layers"] for s in per_shape)
+    pro_gbs = pro_bytes / (ms_pro * 1e-3) / 1e9
     traffic = load_traffic(GEMM_SRC)
     achieved = ops_step / (ms_gemm * 1e-3) / 1e12
     out = {
@@ -540,8 +625,14 @@ def main():
         "stages": {
             "prologue_ms_per_step": round(ms_pro, 4),
             "prologue_avg_launch_us": round(ms_pro * 1e3 / n_launch, 3),
+            "prologue_gbs": round(pro_gbs, 1),
+            "prologue_gbs_note": "algorithmic bytes 3MK + 4M per launch; operands of M = 1024 stay in the "
+                                 "memory-side cache (MALL-resident), so this is not an HBM rate",
+            "prologue_hbm_scale": pro_large,
+            "device_copy_gbs": copy_gbs,
             "gemm_ms_per_step": round(ms_gemm, 4),
         },
+        "device_peak": device_peak_int8_tops(dev.index or 0),
         "per_shape": shape_rows,
         "weighted_total_ms": round(sum(r["w8a8_us"] * r["layers"] for r in shape_rows) / 1e3, 4),
         "compare": compare,
