@@ -49,7 +49,7 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
                 int8_t* __restrict__ QX, float* __restrict__ sX, __half* __restrict__ X16,
                 int* __restrict__ rowexp) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ uint32_t rowmax[16];             // per row: max |X_rot| as fp32 bits (non-negative: uint order)
+  __shared__ uint32_t rowmax[16];             // per row: max |fp32(16 X_rot)| as bits (non-negative: uint order)
   __shared__ unsigned long long rowmax64[16]; // the same as fp64 bits (row-scaled mode)
 
   const int tid = threadIdx.x;
@@ -137,7 +137,7 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
       rotate_group<kBF16>(xrow + (int64_t)g * kGroup, slot, lane, y);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        f[i] = (float)(y[i] * 0.0625);  // exact scaling, single rounding to fp32
+        f[i] = (float)y[i];   // fp32(16 X_rot): the single rounding
         amax = fmaxf(amax, fabsf(f[i]));
       }
     }
@@ -147,8 +147,13 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
   if (active && lane == 0) atomicMax(&rowmax[row_in_wg], __float_as_uint(amax));
   __syncthreads();
   if (!active) return;
-  const float s = __uint_as_float(rowmax[row_in_wg]) / 127.0f;  // IEEE fp32 division
-  if (slot_id == row_in_wg * sp.gpc && lane == 0) sX[row] = s;
+  // The factor 16 of the unnormalised transform stays in the values: with
+  // F = fp32(16 X_rot) = 16 fp32(X_rot) and S = fp32(max|F|) / 127 (IEEE fp32
+  // division) = 16 s_X -- scaling by 2^4 commutes with fp32 rounding, every
+  // nonzero value here being at least 2^-35, far above the subnormals --
+  // F / S equals X_rot / s_X exactly, so the codes are the same.
+  const float s = __uint_as_float(rowmax[row_in_wg]) / 127.0f;
+  if (slot_id == row_in_wg * sp.gpc && lane == 0) sX[row] = s * 0.0625f;   // exact
 
   // pass 2: quantise and store
   for (int c = 0; c < sp.chunks; ++c) {
@@ -157,7 +162,7 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
     if (sp.chunks > 1) {
       rotate_group<kBF16>(xrow + (int64_t)g * kGroup, slot, lane, y);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) f[i] = (float)(y[i] * 0.0625);
+      for (int i = 0; i < 16; ++i) f[i] = (float)y[i];
     }
     const uint4 packed = quantize16(f, s);
     *reinterpret_cast<uint4*>(QX + row * K + (int64_t)g * kGroup + 16 * lane) = packed;

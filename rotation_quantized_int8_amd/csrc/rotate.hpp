@@ -114,35 +114,37 @@ __device__ __forceinline__ void rotate_group(const __half* __restrict__ src, cha
 // q = round_half_even(fp32(v / s)).  The fast path multiplies by the
 // reciprocal; when any product lies within 3e-5 of a half-integer -- closer
 // than its possible deviation from the correctly rounded quotient -- the
-// lane falls back to IEEE division for its 16 values.
+// lane falls back to IEEE division for its 16 values.  The rounding to an
+// integer is one fp32 addition of 1.5 * 2^23: for |t| < 2^22 the sum rounds
+// t half to even at the units place and holds the integer, two's complement,
+// in its low mantissa bits, so the low byte of the sum's bits is the int8
+// code.  |v / s| <= 127 (1 + 2^-23) for finite inputs, so no clamp is needed.
 __device__ __forceinline__ uint4 quantize16(const float (&v)[16], float s) {
-  float q[16];
+  constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+  uint32_t b[16];
   if (s == 0.0f) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = 0.0f;
+    for (int i = 0; i < 16; ++i) b[i] = 0u;
   } else {
     const float rcp = 1.0f / s;
     bool near_tie = false;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float t = v[i] * rcp;
-      q[i] = rintf(t);
-      near_tie |= fabsf(t - q[i]) > 0.49997f;
+      const float t = __fmul_rn(v[i], rcp);
+      const float m = __fadd_rn(t, kMagic);
+      near_tie |= fabsf(__fsub_rn(t, __fsub_rn(m, kMagic))) > 0.49997f;
+      b[i] = __float_as_uint(m);
     }
     if (near_tie) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = rintf(v[i] / s);
+      for (int i = 0; i < 16; ++i) b[i] = __float_as_uint(__fadd_rn(v[i] / s, kMagic));
     }
   }
   uint32_t w[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t b0 = (uint32_t)(int)fminf(fmaxf(q[4 * j + 0], -128.f), 127.f) & 0xffu;
-    uint32_t b1 = (uint32_t)(int)fminf(fmaxf(q[4 * j + 1], -128.f), 127.f) & 0xffu;
-    uint32_t b2 = (uint32_t)(int)fminf(fmaxf(q[4 * j + 2], -128.f), 127.f) & 0xffu;
-    uint32_t b3 = (uint32_t)(int)fminf(fmaxf(q[4 * j + 3], -128.f), 127.f) & 0xffu;
-    w[j] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-  }
+  for (int j = 0; j < 4; ++j)
+    w[j] = (b[4 * j] & 0xffu) | ((b[4 * j + 1] & 0xffu) << 8) | ((b[4 * j + 2] & 0xffu) << 16) |
+           (b[4 * j + 3] << 24);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 

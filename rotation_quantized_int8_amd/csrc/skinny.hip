@@ -153,7 +153,7 @@ skinny_kernel(GemmArgs p, const __half* __restrict__ Xf, int64_t kr, int rpb, in
           float amax = 0.0f;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            f[t][i] = (float)(y[i] * 0.0625);   // exact scaling, single rounding to fp32
+            f[t][i] = (float)y[i];   // fp32(16 X_rot): the single rounding
             amax = fmaxf(amax, fabsf(f[t][i]));
           }
           amax = warp_max16(amax);
@@ -170,8 +170,11 @@ skinny_kernel(GemmArgs p, const __half* __restrict__ Xf, int64_t kr, int rpb, in
           const int m = j / G, g = j - m * G;
           float rmax = 0.0f;
           for (int q = 0; q < G; ++q) rmax = fmaxf(rmax, jmax[m * G + q]);
+          // S = fp32(max|16 X_rot|) / 127 = 16 s_X exactly (power-of-two
+          // scaling commutes with the fp32 roundings of normal values) and
+          // the codes round(F / S) equal round(X_rot / s_X)
           const float s = rmax / 127.0f;                    // IEEE fp32 division
-          if (g == 0 && l16 == 0) srow[m] = s;
+          if (g == 0 && l16 == 0) srow[m] = s * 0.0625f;    // s_X, exact
           *reinterpret_cast<uint4*>(qx + (int64_t)m * K + (int64_t)g * kGroup + 16 * l16) = quantize16(f[t], s);
         }
       }
