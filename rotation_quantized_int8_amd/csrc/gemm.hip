@@ -15,6 +15,9 @@ namespace convrot {
 // With few rows (M <= 128) the int8 product streams the weights: the widest
 // of 64x64, 32x64 and 16x64 (256-byte K slices, 6 stages) tiles that still
 // gives at least 192 workgroups, else 16x64; the other products use 32x64.
+// A narrow int8 product (32x64 tiles leaving CUs idle, e.g. N = 256 at
+// M = 1024) takes 32x32 tiles with 256-byte K slices: one tile per CU and
+// half as many slice barriers.
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
   (void)K;
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
@@ -27,6 +30,8 @@ int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
   if (tiles(256, 128) >= 160) return 13;
   if (tiles(128, 64) >= 128) return 8;
   if (tiles(64, 64) >= 128) return 10;
+  const bool int8 = mode == GemmMode::kI8toF16 || mode == GemmMode::kI8toI32;
+  if (int8 && tiles(32, 64) < 256) return 19;
   return 9;
 }
 
