@@ -12,20 +12,21 @@ namespace convrot {
 // 128x64 tiles spread the work wider, and when even those would leave half
 // the CUs idle, 64x64 or 32x64 tiles do.  The 256x128 tile runs as 8 waves
 // of 64x64 (two per SIMD, so one wave's waits overlap the other's MFMAs).
-// With few rows (M <= 128) the int8 product streams the weights: the widest
-// of 64x64, 32x64 and 16x64 (256-byte K slices, 6 stages) tiles that still
-// gives at least 192 workgroups, else 16x64; the other products use 32x64.
 // A narrow int8 product (32x64 tiles leaving CUs idle, e.g. N = 256 at
 // M = 1024) takes 32x32 tiles with 256-byte K slices: one tile per CU and
 // half as many slice barriers.
+// With few rows (M <= 128) the int8 product streams the weights: 64x64
+// tiles when they still give at least 192 workgroups, else 32x32 tiles with
+// 256-byte K slices (measured ahead of 32x64, 16x64 and 64x32 tiles at every
+// row count from 2 to 128 on the sweep's large shapes); the other products
+// use 32x64.
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
   (void)K;
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (M <= 128) {
     if (mode != GemmMode::kI8toF16 && mode != GemmMode::kI8toI32) return 9;
     if (tiles(64, 64) >= 192) return 10;
-    if (tiles(32, 64) >= 192) return 9;
-    return 15;
+    return 19;
   }
   if (tiles(256, 128) >= 160) return 13;
   if (tiles(128, 64) >= 128) return 8;
@@ -42,8 +43,8 @@ int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
 int64_t w8a8_splits(int64_t M, int64_t N, int64_t K) {
   if (M > 128) return 1;
   const int cfg = choose_gemm_cfg(GemmMode::kI8toI32, M, N, K);
-  const int64_t bm = cfg == 10 ? 64 : cfg == 9 ? 32 : 16;
-  const int64_t tiles = ((M + bm - 1) / bm) * ((N + 63) / 64);
+  const int64_t bm = cfg == 10 ? 64 : 32, bn = cfg == 10 ? 64 : 32;
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   if (tiles >= 32) return 1;
   int64_t s = 1;
   while (tiles * s * 2 <= 128 && K % (s * 2 * 256) == 0 && K / (s * 2) >= 2048) s *= 2;
@@ -57,7 +58,7 @@ int64_t w8a8_splits(int64_t M, int64_t N, int64_t K) {
 W8A8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, bool lora) {
   if (!lora && skinny_fusable(M, K)) return {W8A8Plan::kFused, 1, false};
   if (M <= 16 && N <= 4096) {
-    const int64_t s = skinny_splits(N, K);
+    const int64_t s = skinny_splits(M, N, K);
     return {W8A8Plan::kSkinny, s, lora || s > 1};
   }
   const int64_t s = w8a8_splits(M, N, K);
@@ -98,7 +99,9 @@ splitk_epilogue_kernel(const int32_t* __restrict__ parts, int64_t splits, GemmAr
         if (vec) {
           v[u] = *reinterpret_cast<const v4i*>(src);
         } else {
-          for (int c = 0; c < cols; ++c) v[u][c] = src[c];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (c < cols) v[u][c] = src[c];
         }
       }
     }
@@ -108,33 +111,41 @@ splitk_epilogue_kernel(const int32_t* __restrict__ parts, int64_t splits, GemmAr
       for (int c = 0; c < 4; ++c) a[c] += v[u][c];
   }
 
+  // Columns past N (a ragged tail) are computed on the last column and not
+  // stored.  Every per-column array is indexed by unrolled constants only: a
+  // data-dependent index would make the compiler move the array to LDS,
+  // which made this kernel several times slower.
   float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int r = 0; r < p.t_ld; ++r) {
     const float t = __half2float(p.T[m * p.t_ld + r]);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (c < cols) l[c] = fmaf(t, __half2float(p.U[(n0 + c) * p.t_ld + r]), l[c]);
+    for (int c = 0; c < 4; ++c) {
+      const int64_t n = n0 + c < N ? n0 + c : N - 1;
+      l[c] = fmaf(t, __half2float(p.U[n * p.t_ld + r]), l[c]);
+    }
   }
   __half* Y = reinterpret_cast<__half*>(p.out);
   const float sx = p.sX[m];
-  __half h[4];
+  uint32_t hb[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    if (c >= cols) break;
-    const int64_t n = n0 + c;
+    const int64_t n = n0 + c < N ? n0 + c : N - 1;
     float y = __fmul_rn((float)a[c], __fmul_rn(sx, p.sW[n]));
     if (p.bias) y = __fadd_rn(y, p.bias[n]);
     if (p.t_ld > 0) y = __fadd_rn(y, l[c]);
-    h[c] = __float2half_rn(y);
-    if (p.R) h[c] = __float2half_rn(__half2float(h[c]) + __half2float(p.R[m * N + n]));
+    __half h = __float2half_rn(y);
+    if (p.R) h = __float2half_rn(__half2float(h) + __half2float(p.R[m * N + n]));
+    hb[c] = __half_as_ushort(h);
   }
   if (vec) {
     uint2 o;
-    o.x = (uint32_t)__half_as_ushort(h[0]) | ((uint32_t)__half_as_ushort(h[1]) << 16);
-    o.y = (uint32_t)__half_as_ushort(h[2]) | ((uint32_t)__half_as_ushort(h[3]) << 16);
+    o.x = hb[0] | (hb[1] << 16);
+    o.y = hb[2] | (hb[3] << 16);
     *reinterpret_cast<uint2*>(Y + m * N + n0) = o;
   } else {
-    for (int c = 0; c < cols; ++c) Y[m * N + n0 + c] = h[c];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (c < cols) Y[m * N + n0 + c] = __ushort_as_half((uint16_t)hb[c]);
   }
 }
 

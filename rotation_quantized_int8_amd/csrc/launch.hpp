@@ -36,19 +36,20 @@ int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K);
 // Few-row W8A8 product (M <= 32): K ranges for a size, and the launch
 // (parts == nullptr: one range and the scale epilogue [+ bias, residual] in
 // the kernel; else int32 partials [splits, M, N] for launch_splitk_epilogue).
-int64_t skinny_splits(int64_t N, int64_t K);
+int64_t skinny_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_skinny(const GemmArgs& a, int64_t splits, int32_t* parts, hipStream_t stream);
 // The whole W8A8 layer in one launch for M K <= 8192 (every workgroup
 // quantises the activations X fp16 [M, K] itself); a.X is unused.
 bool skinny_fusable(int64_t M, int64_t K);
 hipError_t launch_skinny_fused(const GemmArgs& a, const void* X, hipStream_t stream);
 
-// Split-K plan of the W8A8 GEMM path (M > 32): number of K splits (1 = none).
+// Split-K plan of the W8A8 tiled-GEMM path with few rows (M <= 128; 1 = no
+// split, always for more rows).
 int64_t w8a8_splits(int64_t M, int64_t N, int64_t K);
 
 // How the W8A8 linear runs for a size: one fused launch (few rows, short
-// rows, no LoRA), the prologue and the few-row kernel (M <= 32), or the
-// prologue and the tiled GEMM; `parts` says whether int32 partials
+// rows, no LoRA), the prologue and the few-row kernel (M <= 16, N <= 4096),
+// or the prologue and the tiled GEMM; `parts` says whether int32 partials
 // [splits, M, N] go through the workspace to the K-split epilogue.
 struct W8A8Plan {
   enum Kind { kFused, kSkinny, kGemm } kind;

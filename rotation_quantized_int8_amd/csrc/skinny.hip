@@ -290,11 +290,14 @@ hipError_t launch_w(const GemmArgs& a, const __half* Xf, int64_t splits, int32_t
 bool skinny_fusable(int64_t M, int64_t K) { return M >= 1 && M <= 16 && M * (K / kGroup) <= kFusedJobs; }
 
 // K ranges for the unfused few-row kernel: split only while the 8-row
-// blocks cover fewer than 128 CUs, each range a multiple of 256 K values.
-int64_t skinny_splits(int64_t N, int64_t K) {
+// blocks cover fewer than 128 CUs and a workgroup would still stream more
+// than 64 KiB of weight and activation bytes (below that the split's second
+// launch costs more than it saves), each range a multiple of 256 K values
+// and at least 1024 long.
+int64_t skinny_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t blocks = (N + 7) / 8;
   int64_t s = 1;
-  while (blocks * s < 128 && K % (s * 2 * 256) == 0 && K / (s * 2) >= 1024) s *= 2;
+  while (blocks * s < 128 && K % (s * 2 * 256) == 0 && K / (s * 2) >= 1024 && (8 + M) * (K / s) > 65536) s *= 2;
   return s;
 }
 
