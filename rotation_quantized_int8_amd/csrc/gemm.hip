@@ -36,28 +36,33 @@ int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
   return 9;
 }
 
-// W8A8 through the tiled GEMM with few rows: when even the chosen tiles
-// give fewer than 32 workgroups, K is split so that tiles x splits reaches
-// about 128 with at least 2048 K values each.  The int32 partial sums are
-// exact, so the split result is bit-identical to the unsplit one.
+// W8A8 through the tiled GEMM with few rows.  K is split only when a
+// workgroup would stream at least 512 KiB of operands (32x32 tiles at
+// K >= 8192) and the tiles fill at most a quarter of the CUs, so that four or
+// more K ranges are possible: below that, the second launch (the split
+// epilogue, about 3 us in a graph) costs more than the shorter ranges save.
+// Splits double while tiles x splits stays within 256 workgroups and each
+// range keeps at least 1024 K values.  The int32 partial sums are exact, so
+// the split result is bit-identical to the unsplit one.
 int64_t w8a8_splits(int64_t M, int64_t N, int64_t K) {
   if (M > 128) return 1;
   const int cfg = choose_gemm_cfg(GemmMode::kI8toI32, M, N, K);
   const int64_t bm = cfg == 10 ? 64 : 32, bn = cfg == 10 ? 64 : 32;
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  if (tiles >= 32) return 1;
+  if (tiles > 64 || (bm + bn) * K < (512 << 10)) return 1;
   int64_t s = 1;
-  while (tiles * s * 2 <= 128 && K % (s * 2 * 256) == 0 && K / (s * 2) >= 2048) s *= 2;
+  while (tiles * s * 2 <= 256 && K % (s * 2 * 256) == 0 && K / (s * 2) >= 1024) s *= 2;
   return s;
 }
 
 // Few rows: one fused launch when every workgroup can quantise the rows
-// itself; up to 16 rows and at most 4096 outputs per row, the few-row kernel
-// (16-row weight blocks leave the tiled GEMM too few workgroups there);
+// itself; up to 8 rows and at most 4096 outputs per row, the few-row kernel
+// (it re-reads the activation rows for every 8 weight rows, which stops
+// paying beyond 8 rows: there the 32x32-tile GEMM is as fast or faster);
 // otherwise the tiled GEMM.
 W8A8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, bool lora) {
   if (!lora && skinny_fusable(M, K)) return {W8A8Plan::kFused, 1, false};
-  if (M <= 16 && N <= 4096) {
+  if (M <= 8 && N <= 4096) {
     const int64_t s = skinny_splits(M, N, K);
     return {W8A8Plan::kSkinny, s, lora || s > 1};
   }

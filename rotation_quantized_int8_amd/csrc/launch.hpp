@@ -48,7 +48,7 @@ hipError_t launch_skinny_fused(const GemmArgs& a, const void* X, hipStream_t str
 int64_t w8a8_splits(int64_t M, int64_t N, int64_t K);
 
 // How the W8A8 linear runs for a size: one fused launch (few rows, short
-// rows, no LoRA), the prologue and the few-row kernel (M <= 16, N <= 4096),
+// rows, no LoRA), the prologue and the few-row kernel (M <= 8, N <= 4096),
 // or the prologue and the tiled GEMM; `parts` says whether int32 partials
 // [splits, M, N] go through the workspace to the K-split epilogue.
 struct W8A8Plan {

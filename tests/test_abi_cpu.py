@@ -42,13 +42,21 @@ def test_workspace_bytes(L):
     # W8A16 with LoRA: X16, T fp16 [M, 32], U' fp16 [N, 32] (256-byte pieces)
     assert L.convrot_workspace_bytes(1, 4, 8, 256, 32) == 2048 + 256 + 512
     assert L.convrot_workspace_bytes(0, 0, 5, 256, 0) == 0
-    # few rows: the few-row kernel covers 2048 outputs without splitting K ...
-    assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 0) == 16 * 8192 + 256
-    # ... but 256 outputs get 4 K ranges of int32 partials
-    assert L.convrot_workspace_bytes(0, 16, 256, 8192, 0) == 16 * 8192 + 256 + 4 * 16 * 256 * 4
-    # with a LoRA the few-row product always goes through int32 partials
+    # few rows: with 16 rows the 32x32-tile GEMM streams 512 KiB per tile at
+    # K = 8192 over only 64 tiles, so K is split 4 ways into int32 partials ...
+    assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 0) == 16 * 8192 + 256 + 4 * 16 * 2048 * 4
+    # ... and 8 ways for 256 outputs (8 tiles; ranges of at least 1024)
+    assert L.convrot_workspace_bytes(0, 16, 256, 8192, 0) == 16 * 8192 + 256 + 8 * 16 * 256 * 4
+    # up to 8 rows the few-row kernel: 2048 outputs need no K split ...
+    assert L.convrot_workspace_bytes(0, 4, 2048, 8192, 0) == 4 * 8192 + 256
+    # ... 256 outputs get 2 K ranges (a workgroup would stream > 64 KiB)
+    assert L.convrot_workspace_bytes(0, 4, 256, 8192, 0) == 4 * 8192 + 256 + 2 * 4 * 256 * 4
+    # with a LoRA the few-row kernel always goes through int32 partials
+    assert L.convrot_workspace_bytes(0, 4, 2048, 8192, 32) == \
+        4 * 8192 + 256 + 4 * 2048 * 4 + 4 * 32 * 2 + 2048 * 32 * 2 + 32 * 4 * 32 * 4
+    # the K-split GEMM with a LoRA
     assert L.convrot_workspace_bytes(0, 16, 2048, 8192, 32) == \
-        16 * 8192 + 256 + 16 * 2048 * 4 + 16 * 32 * 2 + 2048 * 32 * 2 + 32 * 16 * 32 * 4
+        16 * 8192 + 256 + 4 * 16 * 2048 * 4 + 16 * 32 * 2 + 2048 * 32 * 2 + 32 * 16 * 32 * 4
     # a LoRA adds its fp16 low-rank activation [M, t_ld], the fp16 scaled up
     # weight [N, t_ld] (t_ld = rank rounded up to 32) and, when K spans
     # several 256-column chunks, fp32 partial sums per K range
