@@ -140,17 +140,27 @@ lora_down_kernel(const __half* __restrict__ X, const float* __restrict__ D, cons
   }
 }
 
-// T[m, r..r+3] = fp16(sum over K ranges z in order of P[z, m, r..r+3])
+// T[m, r..r+3] = fp16(sum over K ranges z in order of P[z, m, r..r+3]).
+// The ranges' pieces are loaded kBatch at a time, all in flight together,
+// and then added in range order.
 __global__ void __launch_bounds__(256)
 lora_sum_kernel(const float* __restrict__ P, int64_t splits, int64_t M, int t_ld, int rank,
                 __half* __restrict__ T) {
+  constexpr int kBatch = 8;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int q = t_ld / 4;
   if (e >= M * q) return;
   const int64_t m = e / q;
   const int r = 4 * (int)(e - m * q);
-  v4f s = *reinterpret_cast<const v4f*>(P + m * t_ld + r);
-  for (int64_t z = 1; z < splits; ++z) s += *reinterpret_cast<const v4f*>(P + (z * M + m) * t_ld + r);
+  v4f s = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int64_t z0 = 0; z0 < splits; z0 += kBatch) {
+    v4f v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      v[u] = z0 + u < splits ? *reinterpret_cast<const v4f*>(P + ((z0 + u) * M + m) * t_ld + r) : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) s += v[u];
+  }
   v4h h;
 #pragma unroll
   for (int i = 0; i < 4; ++i) h[i] = (_Float16)(r + i < rank ? s[i] : 0.0f);
