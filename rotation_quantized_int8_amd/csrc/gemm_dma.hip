@@ -604,11 +604,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)ST * ((size_t)BM * XS + (size_t)BN * kRowW);
   auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST, XS, EXTRA>;
   if (lds > 160 * 1024) return hipErrorInvalidValue;   // more than one CU's LDS
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(fn), lds); e != hipSuccess) return e;
   const unsigned splits = a.kc ? (unsigned)(a.K / a.kc) : 1u;
   hipLaunchKernelGGL(fn, dim3((unsigned)tiles, splits), dim3(64 * WAM * WAN), lds, stream, a);
   return hipGetLastError();

@@ -33,7 +33,7 @@ template <GemmMode MODE>
 hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream);
 int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K);
 
-// Few-row W8A8 product (M <= 32): K ranges for a size, and the launch
+// Few-row W8A8 product (M <= 16): K ranges for a size, and the launch
 // (parts == nullptr: one range and the scale epilogue [+ bias, residual] in
 // the kernel; else int32 partials [splits, M, N] for launch_splitk_epilogue).
 int64_t skinny_splits(int64_t M, int64_t N, int64_t K);
@@ -84,6 +84,11 @@ int64_t lora_splits(int64_t K);
 hipError_t launch_lora_prep(const void* X, const float* down, const float* up, float scale, int64_t M,
                             int64_t N, int64_t K, int rank, int t_ld, float* P, __half* T, __half* U,
                             hipStream_t stream);
+
+// Lets kernel `fn` use `bytes` of dynamic LDS on the current device (above
+// the 64 KiB default), calling hipFuncSetAttribute only when this kernel has
+// not yet been allowed that much on this device.
+hipError_t allow_dynamic_lds(const void* fn, size_t bytes);
 
 // Empty contractions (K = 0).  Y [M, N] = +0 + bias[n] (or +0) rounded to
 // the output type, then the residual R (same type, may be Y) added once;

@@ -197,11 +197,7 @@ hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __
   const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
   const size_t lds = (size_t)(threads / 16) * kSlotBytes;
   auto fn = &prologue_kernel<kMode, kBF16>;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(fn), lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), lds, stream,
                      reinterpret_cast<const uint16_t*>(X), M, K, sp, QX, sX, X16, rowexp);
   return hipGetLastError();

@@ -1,9 +1,9 @@
-// W8A8 product for few activation rows (M <= 32): the weight-streaming
+// W8A8 product for few activation rows (M <= 16): the weight-streaming
 // regime of the row-count sweep on the page "INT8ConvRot GEMM vs fp16 on M1
 // Max with Metal, MPSMatrix, and MLX (fp16 Wins)" (section "What changed in
 // the computation": A = Q_X Q_W^T in int32, Y = A (.) s_X s_W^T).
 //
-// With M <= 32 the int8 weights are almost all of the traffic (N K bytes
+// With M <= 16 the int8 weights are almost all of the traffic (N K bytes
 // against M K activation bytes), so the kernel is organised around streaming
 // them: a workgroup of W wavefronts owns 16 weight rows and a K range, each
 // wavefront a contiguous 1/W of that range (W grows with K so that a
@@ -302,9 +302,8 @@ int64_t skinny_splits(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_skinny(const GemmArgs& a, int64_t splits, int32_t* parts, hipStream_t stream) {
-  if (a.M > 32 || a.K % (splits * 256) != 0 || (splits > 1 && !parts)) return hipErrorInvalidValue;
-  if (a.M <= 16) return launch_w<1, false>(a, nullptr, splits, parts, stream);
-  return launch_w<2, false>(a, nullptr, splits, parts, stream);
+  if (a.M > 16 || a.K % (splits * 256) != 0 || (splits > 1 && !parts)) return hipErrorInvalidValue;
+  return launch_w<1, false>(a, nullptr, splits, parts, stream);
 }
 
 hipError_t launch_skinny_fused(const GemmArgs& a, const void* X, hipStream_t stream) {

@@ -599,7 +599,8 @@ def test_linear_dequant_within_tolerance(M, N, K, bias):
                                         (16, 2048, 8192, True), (32, 8192, 2048, False), (17, 300, 4096, True),
                                         (8, 256, 8192, False), (24, 1000, 1024, True), (1, 256, 131072, False),
                                         (24, 64, 65536, True), (100, 128, 16384, False), (128, 8192, 2048, True),
-                                        (64, 6144, 256, False)])
+                                        (64, 6144, 256, False), (8, 4096, 4096, True), (9, 4096, 4096, False),
+                                        (12, 1024, 8192, True), (300, 256, 2048, False)])
 def test_linear_w8a8_few_rows_bitexact(M, N, K, bias):
     _say(f"linear w8a8 few rows M={M} N={N} K={K} bias={bias}")
     mism, emax, rel = _w8a8_case(M, N, K, seed=3 * M + K, bias=bias)
