@@ -819,3 +819,46 @@ def test_empty_contraction_every_entry_point():
     assert cr.dequantize_weights(qw0, sw).shape == (N, 0)
     torch.cuda.synchronize()
     _say("  every entry point bit-exact at K = 0")
+
+
+def test_concurrent_host_threads_on_separate_streams():
+    # the library is documented thread-safe: four host threads issue W8A8 and
+    # weight-only calls on their own streams (own workspaces and outputs);
+    # every result equals the single-threaded one bit for bit
+    import threading
+    _say("concurrent host threads, one stream each")
+    shapes = [(300, 2048, 8192), (64, 6144, 256), (1024, 256, 2048), (5, 2048, 4096)]
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        x = wl.make_activations(M, K, seed=40 + i).to(DEV)
+        qw, sw = cr.quantize_weights(wl.make_weights(N, K, seed=40 + i).to(DEV))
+        cases.append((x, qw, sw))
+    torch.cuda.synchronize()
+    ref = [(cr.linear_w8a8(x, qw, sw), cr.linear_w8a16(x, qw, sw)) for (x, qw, sw) in cases]
+    torch.cuda.synchronize()
+    results, errors = [None] * len(cases), []
+
+    def work(i):
+        try:
+            x, qw, sw = cases[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = []
+                for _ in range(5):
+                    outs = [cr.linear_w8a8(x, qw, sw), cr.linear_w8a16(x, qw, sw)]
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:   # reported below, on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (r8, r16), (g8, g16) in zip(ref, results):
+        assert torch.equal(r8.view(torch.int16), g8.view(torch.int16))
+        assert torch.equal(r16.view(torch.int16), g16.view(torch.int16))
+    _say("  4 threads x 5 calls equal to the single-threaded results")
