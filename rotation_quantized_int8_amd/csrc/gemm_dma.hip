@@ -628,6 +628,7 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
         case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3, true>(a, stream);
         case 15: return launch_cfg<MODE, 1, 4, 1, 1, 6, true, 256>(a, stream);
         case 19: return launch_cfg<MODE, 2, 2, 1, 1, 4, true, 256>(a, stream);
+        case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, true, 256>(a, stream);
         default: return hipErrorInvalidValue;
       }
     }
@@ -653,6 +654,7 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 17: return launch_cfg<MODE, 1, 4, 1, 2, 4, false, 256>(a, stream);  // 16x128
     case 18: return launch_cfg<MODE, 2, 2, 1, 2, 6, false, 256>(a, stream);  // 32x64, 256-byte K slices
     case 19: return launch_cfg<MODE, 2, 2, 1, 1, 4, false, 256>(a, stream);  // 32x32, 256-byte K slices
+    case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, false, 256>(a, stream);  // 128x64, 8 waves, 256-byte K slices
     default: return hipErrorInvalidValue;
   }
 }
