@@ -9,10 +9,12 @@ namespace convrot {
 
 // 256x128 tiles read half the operand bytes per output of 128x64 tiles,
 // which pays once they still give most of the 256 CUs a tile; otherwise
-// 128x64 tiles spread the work wider (for the int8 products as 8 waves of
-// 32x32 with 256-byte K slices: two waves per SIMD and half the slice
-// barriers, 5 % faster than 4 waves of 64x32 on 2048x2048), and when even
-// those would leave half the CUs idle, 64x64 or 32x64 tiles do.  The 256x128 tile runs as 8 waves
+// 128x64 tiles spread the work wider (as 8 waves of 32x32 with 256-byte K
+// slices: two waves per SIMD and half the slice barriers, 5 % faster than 4
+// waves of 64x32 for the int8 product on 2048x2048 and 6-10 % for the fp16
+// one; the weight-only product, which widens its int8 weights per wave,
+// keeps 4 waves), and when even those would leave half the CUs idle, 64x64
+// or 32x64 tiles do.  The 256x128 tile runs as 8 waves
 // of 64x64 (two per SIMD, so one wave's waits overlap the other's MFMAs).
 // A narrow int8 product (32x64 tiles leaving CUs idle, e.g. N = 256 at
 // M = 1024) takes 32x32 tiles with 256-byte K slices: one tile per CU and
@@ -32,7 +34,7 @@ int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
   }
   const bool int8 = mode == GemmMode::kI8toF16 || mode == GemmMode::kI8toI32;
   if (tiles(256, 128) >= 160) return 13;
-  if (tiles(128, 64) >= 128) return int8 ? 20 : 8;
+  if (tiles(128, 64) >= 128) return mode == GemmMode::kW8A16 ? 8 : 20;
   if (tiles(64, 64) >= 128) return 10;
   if (int8 && tiles(32, 64) < 256) return 19;
   return 9;
