@@ -612,49 +612,37 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Configuration table: id -> (wave grid, fragments per wave, pipeline depth).
-// Output tile = (16 FM WAVES_M) x (16 FN WAVES_N) in (M, N).
-// A residual or a LoRA selects the kernels compiled with those epilogue
-// steps (only for the tile configurations the library dispatches to), so
-// the plain kernels carry none of their registers or code.
+// Configuration table: id -> (wave grid, fragments per wave, pipeline depth,
+// K slice bytes); output tile = (16 FM WAVES_M) x (16 FN WAVES_N) in (M, N).
+// Only the configurations choose_gemm_cfg dispatches to are built (ids of
+// configurations measured and dropped are not reused).  A residual, a LoRA,
+// row exponents or a bf16 output select the kernels compiled with those
+// epilogue steps, so the plain kernels carry none of their registers or code.
 template <GemmMode MODE>
 hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
+  const bool extra = a.R || a.t_ld > 0 || a.rowexp || a.out_bf16;
   if constexpr (MODE == GemmMode::kI8toF16 || MODE == GemmMode::kW8A16) {
-    if (a.R || a.t_ld > 0 || a.rowexp || a.out_bf16) {
+    if (extra) {
       switch (cfg) {
         case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4, true>(a, stream);
         case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4, true>(a, stream);
         case 10: return launch_cfg<MODE, 2, 2, 2, 2, 4, true>(a, stream);
         case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3, true>(a, stream);
-        case 15: return launch_cfg<MODE, 1, 4, 1, 1, 6, true, 256>(a, stream);
         case 19: return launch_cfg<MODE, 2, 2, 1, 1, 4, true, 256>(a, stream);
         case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, true, 256>(a, stream);
         default: return hipErrorInvalidValue;
       }
     }
+  } else {
+    if (extra) return hipErrorInvalidValue;
   }
   switch (cfg) {
-    case 0: return launch_cfg<MODE, 2, 2, 4, 4, 3>(a, stream);   // 128x128
-    case 1: return launch_cfg<MODE, 2, 2, 4, 4, 4>(a, stream);   // 128x128, 4 stages
-    case 2: return launch_cfg<MODE, 2, 2, 8, 4, 3>(a, stream);   // 256x128
-    case 3: return launch_cfg<MODE, 2, 2, 4, 8, 3>(a, stream);   // 128x256
-    case 4: return launch_cfg<MODE, 2, 1, 4, 4, 4>(a, stream);   // 128x64 (2 waves)
-    case 5: return launch_cfg<MODE, 1, 2, 4, 4, 4>(a, stream);   // 64x128 (2 waves)
-    case 6: return launch_cfg<MODE, 1, 1, 4, 4, 4>(a, stream);   // 64x64 (1 wave)
-    case 7: return launch_cfg<MODE, 2, 2, 2, 4, 4>(a, stream);   // 64x128
-    case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4>(a, stream);   // 128x64
-    case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4>(a, stream);   // 32x64 (few rows)
+    case 8: return launch_cfg<MODE, 2, 2, 4, 2, 4>(a, stream);   // 128x64, 4 waves of 64x32
+    case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4>(a, stream);   // 32x64
     case 10: return launch_cfg<MODE, 2, 2, 2, 2, 4>(a, stream);  // 64x64
-    case 11: return launch_cfg<MODE, 1, 4, 2, 2, 4>(a, stream);  // 32x128
-    case 12: return launch_cfg<MODE, 1, 4, 2, 4, 3>(a, stream);  // 32x256
-    case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3>(a, stream);  // 256x128, 8 waves
-    case 14: return launch_cfg<MODE, 2, 4, 4, 4, 3>(a, stream);  // 128x256, 8 waves
-    case 15: return launch_cfg<MODE, 1, 4, 1, 1, 6, false, 256>(a, stream);  // 16x64, 256-byte K slices
-    case 16: return launch_cfg<MODE, 1, 4, 1, 1, 7, false, 256>(a, stream);  // 16x64, 7 stages
-    case 17: return launch_cfg<MODE, 1, 4, 1, 2, 4, false, 256>(a, stream);  // 16x128
-    case 18: return launch_cfg<MODE, 2, 2, 1, 2, 6, false, 256>(a, stream);  // 32x64, 256-byte K slices
+    case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3>(a, stream);  // 256x128, 8 waves of 64x64
     case 19: return launch_cfg<MODE, 2, 2, 1, 1, 4, false, 256>(a, stream);  // 32x32, 256-byte K slices
-    case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, false, 256>(a, stream);  // 128x64, 8 waves, 256-byte K slices
+    case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, false, 256>(a, stream);  // 128x64, 8 waves of 32x32, 256-byte K slices
     default: return hipErrorInvalidValue;
   }
 }
