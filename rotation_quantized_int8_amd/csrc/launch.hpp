@@ -89,6 +89,10 @@ hipError_t launch_lora_prep(const void* X, const float* down, const float* up, f
 // the 64 KiB default), calling hipFuncSetAttribute only when this kernel has
 // not yet been allowed that much on this device.
 hipError_t allow_dynamic_lds(const void* fn, size_t bytes);
+// Workgroups of kernel `fn` (with `threads` threads and `lds` bytes of
+// dynamic LDS) that the current device holds at once: CUs x workgroups per
+// CU (remembered per kernel, device and size).
+hipError_t resident_grid(const void* fn, int threads, size_t lds, int64_t* wgs);
 
 // Empty contractions (K = 0).  Y [M, N] = +0 + bias[n] (or +0) rounded to
 // the output type, then the residual R (same type, may be Y) added once;

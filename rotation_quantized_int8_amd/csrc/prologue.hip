@@ -169,6 +169,93 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
   }
 }
 
+// The W8A8 prologue for rows of at most 16384 values (one chunk per row), as
+// a persistent grid: a workgroup walks row blocks b, b + gridDim.x, ... and
+// issues the loads of its next block before it rotates, reduces and
+// quantises the current one, so at large M the memory traffic of one block
+// overlaps the vector work of the previous one.  The row maxima of
+// iteration i go through LDS buffer i % 3; buffer (i + 2) % 3 is cleared
+// after the iteration's barrier, which every thread passes only after its
+// last read of that buffer (iteration i - 1) and before its next atomic on
+// it (iteration i + 2, behind the barrier of iteration i + 1).  Arithmetic
+// as in prologue_kernel.
+__global__ void __launch_bounds__(1024)
+prologue_quant_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
+                      int8_t* __restrict__ QX, float* __restrict__ sX) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ uint32_t rowmax[3][16];   // per row: max |fp32(16 X_rot)| as bits (non-negative: uint order)
+
+  const int tid = threadIdx.x;
+  const int slot_id = tid >> 4;       // group slot in the workgroup
+  const int lane = tid & 15;          // lane within the group
+  const int row_in_wg = slot_id / sp.gpc;
+  const int gi = slot_id - row_in_wg * sp.gpc;   // group of the row (one chunk: all of them)
+  const bool in_wg = row_in_wg < sp.rows_per_wg;
+  char* slot = smem + slot_id * kSlotBytes;
+  const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
+
+  if (tid < 48) rowmax[tid >> 4][tid & 15] = 0u;
+  __syncthreads();
+
+  auto has_row = [&](int64_t b) { return in_wg && b < blocks && b * sp.rows_per_wg + row_in_wg < M; };
+  // Loads are issued by every lane, unconditionally, so that the compiler
+  // counts them exactly and waits only for the block it is about to use:
+  // lanes without a row of block b read the last row of the matrix instead
+  // (in bounds, never used).
+  const int rclamp = row_in_wg < sp.rows_per_wg ? row_in_wg : sp.rows_per_wg - 1;
+  auto src = [&](int64_t b) {
+    int64_t r = b * sp.rows_per_wg + rclamp;
+    r = r < M ? r : M - 1;
+    return reinterpret_cast<const v4i*>(X + r * K + (int64_t)gi * kGroup + 16 * lane);
+  };
+  // One block: issue the loads of block b + gridDim.x into (n0, n1), then
+  // rotate, reduce and quantise block b from (c0, c1).  Two register pairs
+  // alternate between the calls, so no in-flight load is copied (a copy
+  // would make the compiler wait for it, and for this block's stores).
+  auto step = [&](int64_t b, int it, const v4i& c0, const v4i& c1, v4i& n0, v4i& n1) {
+    const bool active = has_row(b);
+    const int64_t row = b * sp.rows_per_wg + row_in_wg;
+    n0 = __builtin_nontemporal_load(src(b + gridDim.x));
+    n1 = __builtin_nontemporal_load(src(b + gridDim.x) + 1);
+    float f[16];
+    float amax = 0.0f;
+    if (active) {
+      double y[16];
+      rotate_loaded(c0, c1, slot, lane, y);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        f[i] = (float)y[i];   // fp32(16 X_rot): the single rounding
+        amax = fmaxf(amax, fabsf(f[i]));
+      }
+    }
+    amax = warp_max16(amax);
+    uint32_t* rm = rowmax[it % 3];
+    if (active && lane == 0) atomicMax(&rm[row_in_wg], __float_as_uint(amax));
+    __syncthreads();
+    if (tid < 16) rowmax[(it + 2) % 3][tid] = 0u;
+    if (active) {
+      // S = fp32(max|16 X_rot|) / 127 = 16 s_X exactly; F / S = X_rot / s_X
+      const float sc = __uint_as_float(rm[row_in_wg]) / 127.0f;
+      if (gi == 0 && lane == 0) sX[row] = sc * 0.0625f;
+      const uint4 packed = quantize16(f, sc);
+      *reinterpret_cast<uint4*>(QX + row * K + (int64_t)gi * kGroup + 16 * lane) = packed;
+    }
+  };
+
+  v4i r0 = v4i{0, 0, 0, 0}, r1 = v4i{0, 0, 0, 0}, q0 = r0, q1 = r1;
+  int64_t b = blockIdx.x;
+  r0 = __builtin_nontemporal_load(src(b));
+  r1 = __builtin_nontemporal_load(src(b) + 1);
+  // the same trip count for the whole workgroup (b depends on blockIdx only)
+  for (int it = 0; b < blocks; it += 2) {
+    step(b, it, r0, r1, q0, q1);
+    b += gridDim.x;
+    if (b >= blocks) break;
+    step(b, it + 1, q0, q1, r0, r1);
+    b += gridDim.x;
+  }
+}
+
 Split choose_split(int64_t K) {
   const int G = (int)(K / kGroup);
   Split sp;
@@ -207,7 +294,20 @@ hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __
 
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
                             hipStream_t stream) {
-  return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream);
+  const Split sp = choose_split(K);
+  if (sp.chunks > 1) return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream);
+  const int slots = sp.rows_per_wg * sp.gpc;
+  const int threads = ((slots * 16 + 63) / 64) * 64;
+  const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
+  const size_t lds = (size_t)(threads / 16) * kSlotBytes;
+  const void* fn = reinterpret_cast<const void*>(&prologue_quant_kernel);
+  if (const hipError_t e = allow_dynamic_lds(fn, lds); e != hipSuccess) return e;
+  int64_t resident = 0;
+  if (const hipError_t e = resident_grid(fn, threads, lds, &resident); e != hipSuccess) return e;
+  const int64_t grid = blocks < resident ? blocks : resident;
+  hipLaunchKernelGGL(prologue_quant_kernel, dim3((unsigned)grid), dim3(threads), lds, stream,
+                     reinterpret_cast<const uint16_t*>(X), M, K, sp, QX, sX);
+  return hipGetLastError();
 }
 
 hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
