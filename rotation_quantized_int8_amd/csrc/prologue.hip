@@ -169,21 +169,24 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
   }
 }
 
-// The W8A8 prologue for rows of at most 16384 values (one chunk per row), as
-// a persistent grid: a workgroup walks row blocks b, b + gridDim.x, ... and
-// issues the loads of its next block before it rotates, reduces and
-// quantises the current one, so at large M the memory traffic of one block
-// overlaps the vector work of the previous one.  The row maxima of
-// iteration i go through LDS buffer i % 3; buffer (i + 2) % 3 is cleared
-// after the iteration's barrier, which every thread passes only after its
-// last read of that buffer (iteration i - 1) and before its next atomic on
-// it (iteration i + 2, behind the barrier of iteration i + 1).  Arithmetic
-// as in prologue_kernel.
+// Rows of at most 16384 values (one chunk per row), every mode, as a
+// persistent grid: a workgroup walks row blocks b, b + gridDim.x, ... and
+// issues the loads of its next block before it rotates (and, with a row
+// scale, reduces and quantises or scales) the current one, so at large M
+// the memory traffic of one block overlaps the vector work of the previous
+// one.  Row maxima of iteration i go through LDS buffer i % 3; buffer
+// (i + 2) % 3 is cleared after the iteration's barrier, which every thread
+// passes only after its last read of that buffer (iteration i - 1) and
+// before its next atomic on it (iteration i + 2, behind the barrier of
+// iteration i + 1).  Arithmetic as in prologue_kernel.
+template <int kMode, bool kBF16>
 __global__ void __launch_bounds__(1024)
-prologue_quant_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
-                      int8_t* __restrict__ QX, float* __restrict__ sX) {
+prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
+                           int8_t* __restrict__ QX, float* __restrict__ sX, __half* __restrict__ X16,
+                           int* __restrict__ rowexp) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ uint32_t rowmax[3][16];   // per row: max |fp32(16 X_rot)| as bits (non-negative: uint order)
+  __shared__ uint32_t rowmax[3][16];            // kQuantInt8: max |fp32(16 X_rot)| bits (uint order)
+  __shared__ unsigned long long rowmax64[3][16];  // kRotateScaledF16: max |X_rot| as fp64 bits
 
   const int tid = threadIdx.x;
   const int slot_id = tid >> 4;       // group slot in the workgroup
@@ -194,7 +197,8 @@ prologue_quant_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Spli
   char* slot = smem + slot_id * kSlotBytes;
   const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
 
-  if (tid < 48) rowmax[tid >> 4][tid & 15] = 0u;
+  if (kMode == kQuantInt8 && tid < 48) rowmax[tid >> 4][tid & 15] = 0u;
+  if (kMode == kRotateScaledF16 && tid < 48) rowmax64[tid >> 4][tid & 15] = 0ull;
   __syncthreads();
 
   auto has_row = [&](int64_t b) { return in_wg && b < blocks && b * sp.rows_per_wg + row_in_wg < M; };
@@ -208,37 +212,79 @@ prologue_quant_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Spli
     r = r < M ? r : M - 1;
     return reinterpret_cast<const v4i*>(X + r * K + (int64_t)gi * kGroup + 16 * lane);
   };
+  auto store16 = [&](int64_t row, const __half (&h)[16]) {
+    uint4* dst = reinterpret_cast<uint4*>(X16 + row * K + (int64_t)gi * kGroup + 16 * lane);
+    dst[0] = *reinterpret_cast<const uint4*>(&h[0]);
+    dst[1] = *reinterpret_cast<const uint4*>(&h[8]);
+  };
   // One block: issue the loads of block b + gridDim.x into (n0, n1), then
-  // rotate, reduce and quantise block b from (c0, c1).  Two register pairs
-  // alternate between the calls, so no in-flight load is copied (a copy
-  // would make the compiler wait for it, and for this block's stores).
+  // process block b from (c0, c1).  Two register pairs alternate between the
+  // calls, so no in-flight load is copied (a copy would make the compiler
+  // wait for it, and for this block's stores).
   auto step = [&](int64_t b, int it, const v4i& c0, const v4i& c1, v4i& n0, v4i& n1) {
     const bool active = has_row(b);
     const int64_t row = b * sp.rows_per_wg + row_in_wg;
     n0 = __builtin_nontemporal_load(src(b + gridDim.x));
     n1 = __builtin_nontemporal_load(src(b + gridDim.x) + 1);
-    float f[16];
-    float amax = 0.0f;
-    if (active) {
-      double y[16];
-      rotate_loaded(c0, c1, slot, lane, y);
+    double y[16];
+    if (active) rotate_loaded<kBF16>(c0, c1, slot, lane, y);
+    if constexpr (kMode == kRotateF16) {
+      // weight-only: fp16(X H) per group, no row scale
+      if (active) {
+        __half h[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        f[i] = (float)y[i];   // fp32(16 X_rot): the single rounding
-        amax = fmaxf(amax, fabsf(f[i]));
+        for (int i = 0; i < 16; ++i) h[i] = f64_to_f16_rn(y[i] * 0.0625);
+        store16(row, h);
       }
-    }
-    amax = warp_max16(amax);
-    uint32_t* rm = rowmax[it % 3];
-    if (active && lane == 0) atomicMax(&rm[row_in_wg], __float_as_uint(amax));
-    __syncthreads();
-    if (tid < 16) rowmax[(it + 2) % 3][tid] = 0u;
-    if (active) {
-      // S = fp32(max|16 X_rot|) / 127 = 16 s_X exactly; F / S = X_rot / s_X
-      const float sc = __uint_as_float(rm[row_in_wg]) / 127.0f;
-      if (gi == 0 && lane == 0) sX[row] = sc * 0.0625f;
-      const uint4 packed = quantize16(f, sc);
-      *reinterpret_cast<uint4*>(QX + row * K + (int64_t)gi * kGroup + 16 * lane) = packed;
+    } else if constexpr (kMode == kRotateScaledF16) {
+      // range safe: e = the smallest integer with max |X_rot| <= 2^e (0 for a
+      // zero row), X16 = fp16(X_rot 2^-e) rounded once
+      double amax = 0.0;
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmax(amax, fabs(y[i] * 0.0625));
+      }
+      amax = seg_max_f64(amax);
+      unsigned long long* rm = rowmax64[it % 3];
+      if (active && lane == 0) atomicMax(&rm[row_in_wg], (unsigned long long)__double_as_longlong(amax));
+      __syncthreads();
+      if (tid < 16) rowmax64[(it + 2) % 3][tid] = 0ull;
+      if (active) {
+        const unsigned long long mb = rm[row_in_wg];
+        int e = 0;
+        if (mb != 0ull) {
+          const int ex = (int)((mb >> 52) & 0x7FF) - 1023;
+          e = (mb & ((1ull << 52) - 1)) == 0ull ? ex : ex + 1;
+        }
+        const double down = ldexp(0.0625, -e);   // exact power of two
+        if (gi == 0 && lane == 0) rowexp[row] = e;
+        __half h[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) h[i] = f64_to_f16_rn(y[i] * down);
+        store16(row, h);
+      }
+    } else {
+      float f[16];
+      float amax = 0.0f;
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          f[i] = (float)y[i];   // fp32(16 X_rot): the single rounding
+          amax = fmaxf(amax, fabsf(f[i]));
+        }
+      }
+      amax = warp_max16(amax);
+      uint32_t* rm = rowmax[it % 3];
+      if (active && lane == 0) atomicMax(&rm[row_in_wg], __float_as_uint(amax));
+      __syncthreads();
+      if (tid < 16) rowmax[(it + 2) % 3][tid] = 0u;
+      if (active) {
+        // S = fp32(max|16 X_rot|) / 127 = 16 s_X exactly; F / S = X_rot / s_X
+        const float sc = __uint_as_float(rm[row_in_wg]) / 127.0f;
+        if (gi == 0 && lane == 0) sX[row] = sc * 0.0625f;
+        const uint4 packed = quantize16(f, sc);
+        *reinterpret_cast<uint4*>(QX + row * K + (int64_t)gi * kGroup + 16 * lane) = packed;
+      }
     }
   };
 
@@ -283,6 +329,17 @@ hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __
   const int threads = ((slots * 16 + 63) / 64) * 64;
   const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
   const size_t lds = (size_t)(threads / 16) * kSlotBytes;
+  if (sp.chunks == 1) {   // whole rows: the persistent, pipelined kernel
+    auto fn = &prologue_persistent_kernel<kMode, kBF16>;
+    const void* f = reinterpret_cast<const void*>(fn);
+    if (const hipError_t e = allow_dynamic_lds(f, lds); e != hipSuccess) return e;
+    int64_t resident = 0;
+    if (const hipError_t e = resident_grid(f, threads, lds, &resident); e != hipSuccess) return e;
+    const int64_t grid = blocks < resident ? blocks : resident;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, stream,
+                       reinterpret_cast<const uint16_t*>(X), M, K, sp, QX, sX, X16, rowexp);
+    return hipGetLastError();
+  }
   auto fn = &prologue_kernel<kMode, kBF16>;
   if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(fn), lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), lds, stream,
@@ -294,20 +351,7 @@ hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __
 
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
                             hipStream_t stream) {
-  const Split sp = choose_split(K);
-  if (sp.chunks > 1) return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream);
-  const int slots = sp.rows_per_wg * sp.gpc;
-  const int threads = ((slots * 16 + 63) / 64) * 64;
-  const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
-  const size_t lds = (size_t)(threads / 16) * kSlotBytes;
-  const void* fn = reinterpret_cast<const void*>(&prologue_quant_kernel);
-  if (const hipError_t e = allow_dynamic_lds(fn, lds); e != hipSuccess) return e;
-  int64_t resident = 0;
-  if (const hipError_t e = resident_grid(fn, threads, lds, &resident); e != hipSuccess) return e;
-  const int64_t grid = blocks < resident ? blocks : resident;
-  hipLaunchKernelGGL(prologue_quant_kernel, dim3((unsigned)grid), dim3(threads), lds, stream,
-                     reinterpret_cast<const uint16_t*>(X), M, K, sp, QX, sX);
-  return hipGetLastError();
+  return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream);
 }
 
 hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
