@@ -212,29 +212,57 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
     r = r < M ? r : M - 1;
     return reinterpret_cast<const v4i*>(X + r * K + (int64_t)gi * kGroup + 16 * lane);
   };
-  auto store16 = [&](int64_t row, const __half (&h)[16]) {
-    uint4* dst = reinterpret_cast<uint4*>(X16 + row * K + (int64_t)gi * kGroup + 16 * lane);
-    dst[0] = *reinterpret_cast<const uint4*>(&h[0]);
-    dst[1] = *reinterpret_cast<const uint4*>(&h[8]);
+  // Block b's data (r0, r1) is parked in the segment's LDS slot first; then
+  // the same registers receive the loads of block b + gridDim.x, which are in
+  // flight while block b is rotated and quantised.  A block's results are
+  // held in registers and stored one iteration later, right after the next
+  // loads go out: whatever the compiler makes the next iteration wait for
+  // (it cannot count stores under a branch, so it waits for all memory
+  // operations) was then issued a whole block of work earlier.
+  uint4 pend[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  bool pend_active = false;
+  int64_t pend_row = 0;
+  float pend_s = 0.0f;   // s_X of the held row (kQuantInt8)
+  int pend_e = 0;        // exponent of the held row (kRotateScaledF16)
+  auto flush = [&]() {
+    if (!pend_active) return;
+    if constexpr (kMode == kQuantInt8) {
+      *reinterpret_cast<uint4*>(QX + pend_row * K + (int64_t)gi * kGroup + 16 * lane) = pend[0];
+      if (gi == 0 && lane == 0) sX[pend_row] = pend_s;
+    } else {
+      uint4* dst = reinterpret_cast<uint4*>(X16 + pend_row * K + (int64_t)gi * kGroup + 16 * lane);
+      dst[0] = pend[0];
+      dst[1] = pend[1];
+      if (kMode == kRotateScaledF16 && gi == 0 && lane == 0) rowexp[pend_row] = pend_e;
+    }
   };
-  // One block: issue the loads of block b + gridDim.x into (n0, n1), then
-  // process block b from (c0, c1).  Two register pairs alternate between the
-  // calls, so no in-flight load is copied (a copy would make the compiler
-  // wait for it, and for this block's stores).
-  auto step = [&](int64_t b, int it, const v4i& c0, const v4i& c1, v4i& n0, v4i& n1) {
+
+  v4i r0 = __builtin_nontemporal_load(src(blockIdx.x));
+  v4i r1 = __builtin_nontemporal_load(src(blockIdx.x) + 1);
+  int it = 0;
+  for (int64_t b = blockIdx.x; b < blocks; b += gridDim.x, ++it) {   // uniform trip count
     const bool active = has_row(b);
     const int64_t row = b * sp.rows_per_wg + row_in_wg;
-    n0 = __builtin_nontemporal_load(src(b + gridDim.x));
-    n1 = __builtin_nontemporal_load(src(b + gridDim.x) + 1);
+    if (active) {
+      v4i* st = reinterpret_cast<v4i*>(slot + 32 * lane);
+      st[0] = r0;
+      st[1] = r1;
+    }
+    r0 = __builtin_nontemporal_load(src(b + gridDim.x));
+    r1 = __builtin_nontemporal_load(src(b + gridDim.x) + 1);
+    flush();
+    pend_active = active;
+    pend_row = row;
     double y[16];
-    if (active) rotate_loaded<kBF16>(c0, c1, slot, lane, y);
+    if (active) rotate_staged<kBF16>(slot, lane, y);
     if constexpr (kMode == kRotateF16) {
       // weight-only: fp16(X H) per group, no row scale
       if (active) {
         __half h[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) h[i] = f64_to_f16_rn(y[i] * 0.0625);
-        store16(row, h);
+        pend[0] = *reinterpret_cast<const uint4*>(&h[0]);
+        pend[1] = *reinterpret_cast<const uint4*>(&h[8]);
       }
     } else if constexpr (kMode == kRotateScaledF16) {
       // range safe: e = the smallest integer with max |X_rot| <= 2^e (0 for a
@@ -257,11 +285,12 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
           e = (mb & ((1ull << 52) - 1)) == 0ull ? ex : ex + 1;
         }
         const double down = ldexp(0.0625, -e);   // exact power of two
-        if (gi == 0 && lane == 0) rowexp[row] = e;
         __half h[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) h[i] = f64_to_f16_rn(y[i] * down);
-        store16(row, h);
+        pend[0] = *reinterpret_cast<const uint4*>(&h[0]);
+        pend[1] = *reinterpret_cast<const uint4*>(&h[8]);
+        pend_e = e;
       }
     } else {
       float f[16];
@@ -281,25 +310,12 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
       if (active) {
         // S = fp32(max|16 X_rot|) / 127 = 16 s_X exactly; F / S = X_rot / s_X
         const float sc = __uint_as_float(rm[row_in_wg]) / 127.0f;
-        if (gi == 0 && lane == 0) sX[row] = sc * 0.0625f;
-        const uint4 packed = quantize16(f, sc);
-        *reinterpret_cast<uint4*>(QX + row * K + (int64_t)gi * kGroup + 16 * lane) = packed;
+        pend_s = sc * 0.0625f;
+        pend[0] = quantize16(f, sc);
       }
     }
-  };
-
-  v4i r0 = v4i{0, 0, 0, 0}, r1 = v4i{0, 0, 0, 0}, q0 = r0, q1 = r1;
-  int64_t b = blockIdx.x;
-  r0 = __builtin_nontemporal_load(src(b));
-  r1 = __builtin_nontemporal_load(src(b) + 1);
-  // the same trip count for the whole workgroup (b depends on blockIdx only)
-  for (int it = 0; b < blocks; it += 2) {
-    step(b, it, r0, r1, q0, q1);
-    b += gridDim.x;
-    if (b >= blocks) break;
-    step(b, it + 1, q0, q1, r0, r1);
-    b += gridDim.x;
   }
+  flush();
 }
 
 Split choose_split(int64_t K) {
