@@ -29,8 +29,9 @@
  *   - Every tensor pointer is a device pointer on the current HIP device and
  *     must be 16-byte aligned.  The caller owns every buffer; the library
  *     allocates nothing, frees nothing and keeps no state between calls
- *     beyond per-device caches of the device check and of the kernels'
- *     dynamic-LDS attributes.
+ *     beyond per-device caches of the device check, of the kernels'
+ *     dynamic-LDS attributes and of how many workgroups of a kernel the
+ *     device holds at once.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without synchronising.  All argument checks run on
  *     the host before anything is enqueued; on an error nothing is enqueued
