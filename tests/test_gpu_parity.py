@@ -100,7 +100,11 @@ def _act_compare(x_cpu):
 
 @pytest.mark.parametrize("M,K,dist", [(64, 256, "normal"), (37, 768, "normal"), (300, 2048, "normal"),
                                       (33, 4096, "t3"), (5, 8192, "normal"), (3, 12288, "t3"),
-                                      (3, 20480, "normal"), (2, 131072, "t3"), (1, 256, "normal")])
+                                      (3, 20480, "normal"), (2, 131072, "t3"), (1, 256, "normal"),
+                                      # more row blocks than the device holds at once: workgroups of
+                                      # the persistent prologue walk two or more blocks, the last
+                                      # one ragged
+                                      (16389, 256, "normal"), (2051, 2048, "t3"), (1001, 8192, "normal")])
 def test_act_quant_bitexact(M, K, dist):
     _say(f"act quant M={M} K={K} {dist}")
     x = wl.make_activations(M, K, seed=M * 7 + K, dist=dist)
@@ -862,3 +866,17 @@ def test_concurrent_host_threads_on_separate_streams():
         assert torch.equal(r8.view(torch.int16), g8.view(torch.int16))
         assert torch.equal(r16.view(torch.int16), g16.view(torch.int16))
     _say("  4 threads x 5 calls equal to the single-threaded results")
+
+
+@pytest.mark.parametrize("M,K", [(2051, 2048), (1001, 8192)])
+def test_weight_only_prologues_many_blocks(M, K):
+    # the weight-only and range-safe prologues with more row blocks than
+    # resident workgroups (each workgroup walks several blocks)
+    _say(f"weight-only prologues, many blocks M={M} K={K}")
+    x = wl.make_activations(M, K, seed=M + K)
+    x16 = _np(cr.act_rotate_f16(x.to(DEV)))
+    assert np.array_equal(x16.view(np.uint16), O.rotate_activations_f16(x.numpy()).view(np.uint16))
+    xs, e = cr.act_rotate_scaled(x.to(DEV))
+    xo, eo = O.rotate_rowscaled_f16(x.numpy().astype(np.float32))
+    assert np.array_equal(_np(xs).view(np.uint16), xo.view(np.uint16))
+    assert np.array_equal(_np(e).astype(np.int64), eo)
