@@ -163,14 +163,14 @@ def summarize_pmc(fetch_csv, write_csv):
         "hbm_bytes_per_launch": round(per_launch),
     }
     # the activation prologue of the same run (not the roofline kernel)
-    pf = [v for (k, v) in fetch if "prologue_kernel" in k]
-    pw = [v for (k, v) in write if "prologue_kernel" in k]
+    pf = [v for (k, v) in fetch if "prologue_" in k]
+    pw = [v for (k, v) in write if "prologue_" in k]
     if pf and len(pf) == len(pw):
         import workload as wl
         layers = sum(n for (_, _, n) in wl.LAYER_SHAPES)
         algo = sum((3.0 * wl.M_FIXED * k + 4.0 * wl.M_FIXED) * n for (_, k, n) in wl.LAYER_SHAPES) / layers
         rec["prologue"] = {
-            "kernel": "prologue_kernel",
+            "kernel": "prologue_persistent_kernel",
             "launches": len(pf),
             "fetch_kib_per_launch_raw": round(sum(pf) / len(pf), 1),
             "write_kib_per_launch_raw": round(sum(pw) / len(pw), 1),
