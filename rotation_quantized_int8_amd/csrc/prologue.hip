@@ -12,10 +12,13 @@
 // The rotation (exact fp64 butterflies, one rounding) and the quantisation
 // are the device functions of rotate.hpp.
 
-// Work split.  G = K/256 groups per row.  K <= 4096: a 256-thread workgroup
-// holds floor(16/G) rows.  K <= 16384: one row, 16*G threads.  Longer rows:
-// 1024 threads walk the row in chunks of 64 groups twice (maximum, then
-// quantise), recomputing the transform instead of holding the row.
+// Work split.  G = K/256 groups per row.  K <= 4096: a row block of
+// floor(16/G) rows per 256-thread workgroup; K <= 16384: one row per block,
+// 16*G threads.  These whole-row blocks run in a persistent grid
+// (prologue_persistent_kernel) that loads the next block while it works on
+// the current one.  Longer rows (prologue_kernel): 1024 threads walk the row
+// in chunks of 64 groups twice (maximum, then quantise or scale),
+// recomputing the transform instead of holding the row.
 
 #include "launch.hpp"
 #include "rotate.hpp"
