@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -50,6 +51,9 @@ def parse():
     p.add_argument("--profile-kernels", action="store_true",
                    help="run one eager W8A8 step plus a calibration copy of known size and exit "
                         "(the program to run under rocprofv3 --pmc)")
+    p.add_argument("--counter-means", nargs="+", metavar="CSV",
+                   help="print the mean of every counter per dispatch of each GEMM tile configuration "
+                        "and of the prologue from rocprofv3 --pmc CSVs of a --profile-kernels run, and exit")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
                         "of a --profile-kernels run into profiles/gemm_i8_sweep_traffic.json and exit")
@@ -132,6 +136,32 @@ def _pmc_rows(path, counter):
             if r.get("Counter_Name") == counter:
                 rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
     return rows
+
+
+def counter_means(paths):
+    """Mean of each counter per dispatch, per GEMM instance (its template
+    arguments) and for the prologue, over rocprofv3 --pmc CSV files."""
+    import csv
+    import collections
+    sums = collections.defaultdict(lambda: collections.defaultdict(float))
+    count = collections.defaultdict(collections.Counter)
+    for path in paths:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                k = r["Kernel_Name"]
+                if GEMM_KERNEL in k:
+                    m = re.search(r"gemm_dma_kernel<([^>]*)>", k)
+                    key = "gemm<" + (m.group(1) if m else "?") + ">"
+                elif "prologue_" in k:
+                    key = "prologue"
+                else:
+                    continue
+                sums[key][r["Counter_Name"]] += float(r["Counter_Value"])
+                count[key][r["Counter_Name"]] += 1
+    out = {key: {"dispatches": max(count[key].values()),
+                 **{c: round(v / count[key][c], 1) for c, v in sorted(cs.items())}}
+           for key, cs in sums.items()}
+    print(json.dumps(out, indent=1))
 
 
 def summarize_pmc(fetch_csv, write_csv):
@@ -348,6 +378,9 @@ def cpu_baseline(shapes, M):
 
 def main():
     args = parse()
+    if args.counter_means:
+        counter_means(args.counter_means)
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return

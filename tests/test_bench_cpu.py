@@ -1,0 +1,77 @@
+"""Host-side helpers of bench.py: the counter summaries that feed
+`roofline.traffic` and the per-configuration counter means, run on small
+synthetic rocprofv3-style CSV files, and the single-GPU guard."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+GEMM_A = "void convrot::(anonymous namespace)::gemm_dma_kernel<(convrot::GemmMode)1, 4, 2, 2, 2, 3, 256, false>(x)"
+GEMM_B = "void convrot::(anonymous namespace)::gemm_dma_kernel<(convrot::GemmMode)1, 2, 2, 1, 1, 4, 256, false>(x)"
+PRO = "void convrot::(anonymous namespace)::prologue_persistent_kernel<0, false>(y)"
+COPY = "void at::native::elementwise_kernel<128, 4>(z)"
+
+
+def _write(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (k, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_summarize_pmc_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    kib = 1024.0
+    # the copy reads and writes COPY_BYTES; FETCH_SIZE shows half of its reads
+    fetch = [(COPY, bench.COPY_BYTES / kib / 2), (GEMM_A, 100.0), (GEMM_B, 300.0), (PRO, 10.0)]
+    write = [(COPY, bench.COPY_BYTES / kib), (GEMM_A, 50.0), (GEMM_B, 70.0), (PRO, 4.0)]
+    _write(tmp_path / "f.csv", "FETCH_SIZE", fetch)
+    _write(tmp_path / "w.csv", "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(out))
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    rec = json.loads(out.read_text())
+    assert rec["launches"] == 2
+    assert rec["copy_calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert rec["copy_calibration"]["write_factor"] == pytest.approx(1.0)
+    # per launch: (100 + 300) / 2 KiB read x 2 + (50 + 70) / 2 KiB written x 1
+    assert rec["hbm_bytes_per_launch"] == round((200.0 * 2 + 60.0) * 1024)
+    assert rec["prologue"]["hbm_bytes_per_launch"] == round((10.0 * 2 + 4.0) * 1024)
+    assert rec["source_sha256_16"] == bench.source_hash(bench.GEMM_SRC)
+
+
+def test_summarize_pmc_rejects_mismatched_runs(tmp_path, monkeypatch):
+    _write(tmp_path / "f.csv", "FETCH_SIZE", [(COPY, 1.0), (GEMM_A, 1.0), (GEMM_A, 2.0)])
+    _write(tmp_path / "w.csv", "WRITE_SIZE", [(COPY, 1.0), (GEMM_A, 1.0)])
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "t.json"))
+    with pytest.raises(SystemExit):
+        bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    assert not (tmp_path / "t.json").exists()
+
+
+def test_counter_means_per_configuration(tmp_path, capsys):
+    _write(tmp_path / "a.csv", "SQ_INSTS_MFMA", [(GEMM_A, 10.0), (GEMM_A, 30.0), (GEMM_B, 4.0), (PRO, 0.0),
+                                                 (COPY, 99.0)])
+    _write(tmp_path / "b.csv", "SQ_WAVES", [(GEMM_A, 8.0), (GEMM_A, 8.0), (GEMM_B, 4.0), (PRO, 16.0)])
+    bench.counter_means([str(tmp_path / "a.csv"), str(tmp_path / "b.csv")])
+    out = json.loads(capsys.readouterr().out)
+    a = out["gemm<(convrot::GemmMode)1, 4, 2, 2, 2, 3, 256, false>"]
+    b = out["gemm<(convrot::GemmMode)1, 2, 2, 1, 1, 4, 256, false>"]
+    assert a["SQ_INSTS_MFMA"] == 20.0 and a["SQ_WAVES"] == 8.0 and a["dispatches"] == 2
+    assert b["SQ_INSTS_MFMA"] == 4.0 and b["dispatches"] == 1
+    assert out["prologue"]["SQ_WAVES"] == 16.0
+    assert len(out) == 3      # the copy kernel is not reported
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "single-GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
