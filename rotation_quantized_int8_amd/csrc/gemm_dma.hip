@@ -33,7 +33,8 @@
 // that every later fragment read must wait for.
 //
 // Epilogue: scale and bias operands are fetched at kernel entry; the finished
-// tile is converted in registers, staged through the (now idle) LDS ring and
+// tile is converted in registers, staged through the (now idle) LDS ring (each
+// barrier waits for the wave's own LDS operations first) and
 // written as whole 16-byte chunks of contiguous output rows with
 // non-temporal stores.
 //
@@ -372,7 +373,12 @@ gemm_dma_kernel(GemmArgs p) {
         }
     }
   };
+  // Workgroup barrier.  The hardware barrier does not wait for the wave's
+  // own LDS operations, so lgkmcnt(0) comes first: LDS writes made before
+  // the barrier are visible to every wave after it, and LDS reads made
+  // before it are done before any wave overwrites their addresses.
   auto barrier = [&]() {
+    wait_lgkm0();
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
@@ -410,7 +416,6 @@ gemm_dma_kernel(GemmArgs p) {
     }
     if (kt + STAGES - 1 < nk) wait_vmcnt<kAhead>();
     else wait_vmcnt<0>();
-    wait_lgkm0();
     barrier();
     if (kt + STAGES < nk) issue(kt + STAGES);
     load_frags(0, kt + 1, 0);
@@ -517,7 +522,6 @@ gemm_dma_kernel(GemmArgs p) {
   // stores are whole 16-byte chunks of contiguous output rows.
   constexpr int ROWB = BN * kOut + 16;            // staged row bytes (+16: bank offset per row)
   static_assert(BM * ROWB <= STAGES * (XBYTES + WBYTES), "staging tile must fit in the ring");
-  wait_lgkm0();
   barrier();                                      // every wave is done reading the ring
 #pragma unroll
   for (int i = 0; i < FN; ++i) {

@@ -200,6 +200,31 @@ def test_gemm_i8_f16_bitexact_given_same_inputs(M, N, K, with_bias):
     assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
 
 
+def test_gemm_i8_f16_repeated_launches_every_tile():
+    """Back-to-back launches over shapes that select each int8 tile
+    configuration (256x128, 128x64, 64x64 and 32x32 tiles), interleaved so
+    that the timing of one launch differs from the next; every output must
+    equal the oracle bit for bit.  Guards the ordering of the LDS writes of
+    the staged output tile before the barrier that publishes them."""
+    shapes = [(1024, 6144, 256), (1024, 2048, 2048), (512, 1024, 4096), (128, 6144, 2048), (1024, 256, 2048)]
+    rng = np.random.default_rng(2024)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    cases = []
+    for (M, N, K) in shapes:
+        qx = rng.integers(-127, 128, (M, K), dtype=np.int8)
+        qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
+        sx = (rng.random(M, dtype=np.float32) * np.float32(0.01) + np.float32(1e-4)).astype(np.float32)
+        sw = (rng.random(N, dtype=np.float32) * np.float32(0.001) + np.float32(1e-5)).astype(np.float32)
+        yo = O.epilogue_w8a8(O.int8_gemm(qx, qw), sx, sw, None)
+        cases.append(((M, N, K), t(qx), t(sx), t(qw), t(sw), t(yo.view(np.int16))))
+    for rep in range(12):
+        for (shape, qx, sx, qw, sw, yo) in cases:
+            yg = cr.gemm_i8_f16(qx, sx, qw, sw, None)
+            torch.cuda.synchronize()
+            bad = int((yg.view(torch.int16) != yo).sum())
+            assert bad == 0, f"launch {rep} of M, N, K = {shape}: {bad} elements differ"
+
+
 # ------------------------------------------------- end-to-end W8A8 (a1-a5)
 
 def _e_max(yg, yo, sx, sw, K):
