@@ -215,14 +215,19 @@ def test_gemm_i8_f16_repeated_launches_every_tile():
         qw = rng.integers(-127, 128, (N, K), dtype=np.int8)
         sx = (rng.random(M, dtype=np.float32) * np.float32(0.01) + np.float32(1e-4)).astype(np.float32)
         sw = (rng.random(N, dtype=np.float32) * np.float32(0.001) + np.float32(1e-5)).astype(np.float32)
-        yo = O.epilogue_w8a8(O.int8_gemm(qx, qw), sx, sw, None)
-        cases.append(((M, N, K), t(qx), t(sx), t(qw), t(sw), t(yo.view(np.int16))))
+        ao = O.int8_gemm(qx, qw)
+        yo = O.epilogue_w8a8(ao, sx, sw, None)
+        cases.append(((M, N, K), t(qx), t(sx), t(qw), t(sw), t(yo.view(np.int16)), t(ao.astype(np.int32))))
     for rep in range(12):
-        for (shape, qx, sx, qw, sw, yo) in cases:
+        for (shape, qx, sx, qw, sw, yo, ao) in cases:
             yg = cr.gemm_i8_f16(qx, sx, qw, sw, None)
+            ag = cr.gemm_i8_i32(qx, qw) if rep % 3 == 0 else None   # the int32 tile staging too
             torch.cuda.synchronize()
             bad = int((yg.view(torch.int16) != yo).sum())
-            assert bad == 0, f"launch {rep} of M, N, K = {shape}: {bad} elements differ"
+            assert bad == 0, f"launch {rep} of M, N, K = {shape}: {bad} fp16 elements differ"
+            if ag is not None:
+                bad = int((ag != ao).sum())
+                assert bad == 0, f"launch {rep} of M, N, K = {shape}: {bad} int32 elements differ"
 
 
 # ------------------------------------------------- end-to-end W8A8 (a1-a5)
