@@ -230,6 +230,33 @@ def test_gemm_i8_f16_repeated_launches_every_tile():
                 assert bad == 0, f"launch {rep} of M, N, K = {shape}: {bad} int32 elements differ"
 
 
+@pytest.mark.parametrize("M,N,K", [(4, 8192, 2048), (64, 8192, 2048), (1024, 6144, 256)])
+def test_linear_repeats_are_bit_identical(M, N, K):
+    """The fused few-row, K-split and tiled W8A8 paths, alone and with LoRA
+    and a residual, give the same bits on every repeat while other layers'
+    launches run in between (no result may depend on launch timing)."""
+    _say(f"repeat determinism M={M} N={N} K={K}")
+    x = wl.make_activations(M, K, seed=5).to(DEV)
+    w = wl.make_weights(N, K, seed=6).to(DEV)
+    qw, sw = cr.quantize_weights(w)
+    b = wl.make_bias(N, seed=7).to(DEV)
+    g = torch.Generator().manual_seed(8)
+    r = (torch.randn(M, N, generator=g) * 0.1).half().to(DEV)
+    down = (torch.randn(32, K, generator=g) * 0.02).to(DEV)
+    up = (torch.randn(N, 32, generator=g) * 0.02).to(DEV)
+    xo = wl.make_activations(256, 2048, seed=9).to(DEV)
+    qo, so = cr.quantize_weights(wl.make_weights(2048, 2048, seed=10).to(DEV))
+    paths = [lambda: cr.linear_w8a8(x, qw, sw, b),
+             lambda: cr.linear_w8a8_ex(x, qw, sw, b, lora=(down, up, 0.5), residual=r)]
+    for f in paths:
+        ref = f().view(torch.int16).clone()
+        for rep in range(8):
+            cr.linear_w8a8(xo, qo, so)
+            y = f()
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), ref), f"repeat {rep} differs"
+
+
 # ------------------------------------------------- end-to-end W8A8 (a1-a5)
 
 def _e_max(yg, yo, sx, sw, K):
