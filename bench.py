@@ -282,7 +282,8 @@ M_SWEEP_SHAPES = ((8192, 2048), (2048, 8192))
 
 def m_sweep(cr, L, stream, dev):
     """W8A8 end to end and fp16 F.linear at several row counts on the two large
-    shapes, graph-captured: hot (the same weights every call, median of 5 sets
+    shapes, for N(0,1) and Student-t(3) activations (each with the outlier
+    channels), graph-captured: hot (the same weights every call, median of 5 sets
     of 10 calls, the pages' protocol) and cold (every call its own weight copy,
     the copies together larger than the 256 MB memory-side cache, mean over 3
     replays)."""
@@ -298,8 +299,8 @@ def m_sweep(cr, L, stream, dev):
         del w
         qcold = [qw.clone() for _ in range(max(2, cold_bytes // (N * K)))]
         wcold = [w16.clone() for _ in range(max(2, cold_bytes // (2 * N * K)))]
-        for M in M_SWEEP:
-            x = wl.make_activations(M, K, seed=0).to(dev)
+        for (M, dist) in [(m, "normal") for m in M_SWEEP] + [(m, "t3") for m in M_SWEEP]:
+            x = wl.make_activations(M, K, seed=0, dist=dist).to(dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             ws = torch.empty(cr.workspace_bytes(cr.PATH_W8A8, M, N, K), dtype=torch.uint8, device=dev)
 
@@ -319,7 +320,7 @@ def m_sweep(cr, L, stream, dev):
                         F.linear(x, w_)
                 return run
 
-            row = {"N": N, "K": K, "M": M}
+            row = {"N": N, "K": K, "M": M, "x_dist": dist}
             for name, fn, calls in (("w8a8_us", w8a8_calls([qw] * 10), 10),
                                     ("fp16_torch_linear_us", f16_calls([w16] * 10), 10)):
                 g = capture(fn, stream)
@@ -339,39 +340,88 @@ def m_sweep(cr, L, stream, dev):
     return rows
 
 
+def host_cpu():
+    """Model name, physical cores, logical CPUs and SMT of the host (Linux)."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    logical = os.cpu_count() or 1
+    physical = len(cores) or None
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = logical
+    return {"model": model, "physical_cores": physical, "logical_cpus": logical,
+            "smt_per_core": (logical // physical) if physical else None,
+            "cpus_usable_by_this_process": usable}
+
+
 def cpu_baseline(shapes, M):
-    """The oracle, untuned, on the host: one full M=1024 W8A8 call per shape,
-    weighted by layer count like the GPU metric."""
+    """The oracle, untuned, on the host: full M=1024 W8A8 calls per shape
+    (its four stages timed one by one), weighted by layer count like the GPU
+    metric."""
     import numpy as np
-    import torch
     from oracle import convrot_oracle as O
     import workload as wl
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        threads = os.cpu_count()
     tot_ops, tot_t = 0.0, 0.0
+    stage_tot = {"rotate": 0.0, "quantise": 0.0, "gemm": 0.0, "epilogue": 0.0}
     per = []
     for (N, K, L) in shapes:
         x = wl.make_activations(M, K, seed=0).numpy()
         qw, sw = O.quantize_weights(wl.make_weights(N, K, seed=0).numpy())  # offline, untimed
-        ts = []
-        while len(ts) < 3 or sum(ts) < CPU_SECONDS_PER_SHAPE:
+        runs = []
+        while len(runs) < 3 or sum(r["total"] for r in runs) < CPU_SECONDS_PER_SHAPE:
             t0 = time.perf_counter()
-            O.linear_w8a8(x, qw, sw)
-            ts.append(time.perf_counter() - t0)
-        t = sorted(ts)[len(ts) // 2]
-        per.append({"N": N, "K": K, "seconds": round(t, 4), "runs": len(ts)})
+            xr = O.rotate_activations_f32(x)            # the oracle's W8A8 call, stage by stage
+            t1 = time.perf_counter()
+            qx, sx = O.quantize_rows(xr)
+            t2 = time.perf_counter()
+            a = O.int8_gemm(qx, qw)
+            t3 = time.perf_counter()
+            O.epilogue_w8a8(a, sx, sw)
+            t4 = time.perf_counter()
+            runs.append({"rotate": t1 - t0, "quantise": t2 - t1, "gemm": t3 - t2, "epilogue": t4 - t3,
+                         "total": t4 - t0})
+        med = sorted(runs, key=lambda r: r["total"])[len(runs) // 2]
+        per.append({"N": N, "K": K, "seconds": round(med["total"], 4), "runs": len(runs),
+                    "stages_s": {k: round(med[k], 4) for k in stage_tot}})
         tot_ops += L * 2.0 * M * N * K
-        tot_t += L * t
+        tot_t += L * med["total"]
+        for k in stage_tot:
+            stage_tot[k] += L * med[k]
     return {
-        "value": round(tot_ops / tot_t / 1e12, 4), "unit": "TOPS", "cores": int(cores),
+        "value": round(tot_ops / tot_t / 1e12, 4), "unit": "TOPS", "cores": int(threads),
         "kind": "oracle",
         "sample": "repeated full W8A8 calls (rotate, quantise, int GEMM, epilogue) per shape at M=1024 "
                   f"for >= {CPU_SECONDS_PER_SHAPE} s each (median call), weighted by the 448 layer counts; "
                   "weight prep untimed",
+        "cores_note": "threads of the BLAS pool the oracle's float64/int products ran on; the rest is "
+                      "single-threaded numpy",
+        "host": host_cpu(),
         "per_shape": per,
+        "weighted_stage_s": {k: round(v, 3) for k, v in stage_tot.items()},
         "weighted_total_s": round(tot_t, 3),
     }
 
@@ -485,21 +535,20 @@ def main():
     with torch.cuda.stream(stream):
         g = capture(w8a8_step, stream)
         # the graph's result must equal an eager call, replay after replay
-        ref = {}
         for s in per_shape:
             s["y"].zero_()
-        g.replay()
+        w8a8_step()
         torch.cuda.synchronize()
         ref = [s["y"].clone() for s in per_shape]
-        for _ in range(3):
+        for rep in range(4):
             for s in per_shape:
                 s["y"].zero_()
-            w8a8_step()
+            g.replay()
             torch.cuda.synchronize()
             for s, r in zip(per_shape, ref):
                 if not torch.equal(s["y"].view(torch.int16), r.view(torch.int16)):
-                    raise RuntimeError("graph replay differs from the eager result")
-            g.replay()
+                    raise RuntimeError(f"graph replay {rep} differs from the eager result")
+            w8a8_step()          # eager work between the replays
             torch.cuda.synchronize()
         ms_step = timed_graph(g, args.steps, args.warmup, stream)
         del g
@@ -549,6 +598,8 @@ def main():
                 row[name + "_us"] = round(t * 1e3, 3)
             row["w8a8_tops"] = round(2.0 * M * N * K / (row["w8a8_us"] * 1e-6) / 1e12, 1)
             row["gemm_tops"] = round(2.0 * M * N * K / (row["gemm_i8_f16_us"] * 1e-6) / 1e12, 1)
+            row["gemm_frac_of_int8_peak"] = round(row["gemm_tops"] / PEAK_INT8_TOPS, 4)
+            row["w8a8_frac_of_int8_peak"] = round(row["w8a8_tops"] / PEAK_INT8_TOPS, 4)
             shape_rows.append(row)
 
         compare = {}
@@ -648,10 +699,13 @@ def main():
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": PEAK_INT8_TOPS,
-            "unit": "TFLOP/s",
+            "unit": "TOPS",
             "unit_note": "int8 operations (2MNK) per second, against the dense int8 MFMA peak",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": traffic,
+            "traffic_note": "FETCH_SIZE + WRITE_SIZE per launch, scaled by a copy of known size: the L2's "
+                            "fills and write-backs, served by the memory-side cache (MALL) or HBM; null "
+                            "when the GEMM source differs from the profiled one",
             "avg_launch_us": round(ms_gemm * 1e3 / n_launch, 3),
             "ops_per_launch_avg": ops_step / n_launch,
         },

@@ -213,29 +213,50 @@ convrot_status convrot_act_rotate_scaled(const void* X, int x_dtype, int64_t M, 
 convrot_status convrot_dequantize_weights(const int8_t* Q_W, const float* s_W, int64_t N, int64_t K,
                                           void* W16, void* stream);
 
-/* Prologue alone: X fp16 [M, K] -> Q_X int8 [M, K], s_X fp32 [M]. */
+/* Prologue alone: page "INT8ConvRot GEMM vs fp16 on M1 Max with Metal,
+ * MPSMatrix, and MLX (fp16 Wins)", section "What changed in the computation",
+ * activation equation: X_rot = X H per 256-group, s_X[m] = max_k |X_rot| / 127
+ * over the whole row, Q_X = round(X_rot / s_X).  X fp16 [M, K] -> Q_X int8
+ * [M, K] and s_X fp32 [M] (caller-owned, row-major), bit-exact under the
+ * arithmetic contract above.  Errors as for every entry point; K == 0 writes
+ * s_X = 0. */
 convrot_status convrot_act_quant(const void* X, int64_t M, int64_t K,
                                  int8_t* Q_X, float* s_X, void* stream);
 
-/* Weight-only prologue alone: X fp16 [M, K] -> X16 = fp16(X H) [M, K]. */
+/* Weight-only prologue alone: same page and section, the weight-only
+ * listing (the activations are rotated online and handed over as fp16
+ * x_rot).  X fp16 [M, K] -> X16 fp16 [M, K] = fp16(X H), rounded once from
+ * the exact product (bit-exact).  K == 0 launches nothing. */
 convrot_status convrot_act_rotate_f16(const void* X, int64_t M, int64_t K,
                                       void* X16, void* stream);
 
-/* Integer product alone: A int32 [M, N] = Q_X Q_W^T.  Inputs are expected in
+/* Integer product alone: same page, section "What changed in the
+ * computation", product equation (A = Q_X Q_W^T accumulated in int32; the
+ * section "Running int8xint8 in a Metal kernel" checks exactly this integer
+ * result against a CPU matmul).  Q_X int8 [M, K], Q_W int8 [N, K] -> A int32
+ * [M, N], bit-exact (integer sums, any order).  Inputs are expected in
  * [-127, 127] as the quantisers produce them (with -128 codes A is exact only
- * while 128 * 128 * K < 2^31). */
+ * while 128 * 128 * K < 2^31).  K == 0 writes A = 0. */
 convrot_status convrot_gemm_i8_i32(const int8_t* Q_X, const int8_t* Q_W,
                                    int64_t M, int64_t N, int64_t K,
                                    int32_t* A, void* stream);
 
-/* Integer product with the scale epilogue: Y fp16 [M, N]. */
+/* Integer product with the scale epilogue: same page and section, product
+ * equation Y = A (.) s_X s_W^T.  Q_X int8 [M, K], s_X fp32 [M], Q_W int8
+ * [N, K], s_W fp32 [N], optional bias fp32 [N] -> Y fp16 [M, N] =
+ * fp16(fp32(A) * fp32(s_X[m] * s_W[n]) [+ bias[n]]), bit-exact under the
+ * arithmetic contract above.  K == 0 writes Y = +0 [+ bias]. */
 convrot_status convrot_gemm_i8_f16(const int8_t* Q_X, const float* s_X,
                                    const int8_t* Q_W, const float* s_W, const float* bias,
                                    int64_t M, int64_t N, int64_t K, void* Y, void* stream);
 
-/* fp16 baseline GEMM (the fp16 column of the six-shape table of [P1]):
- * Y fp16 [M, N] = X fp16 [M, K] . W fp16 [N, K]^T, fp32 accumulation.
- * K must be a multiple of 256 here as well (K == 0 gives Y = +0). */
+/* fp16 baseline GEMM: the fp16 column of the six-shape table on the page
+ * "INT8ConvRot GEMM vs fp16 on M1 Max with Metal, MPSMatrix, and MLX (fp16
+ * Wins)", section "Testing the MPS weight-only INT8 path in isolation" (the
+ * comparison point of every table there).  Y fp16 [M, N] = X fp16 [M, K] .
+ * W fp16 [N, K]^T with fp32 accumulation on fp16 MFMA, so Y matches the
+ * exact value within accumulation error, not bit for bit.  K must be a
+ * multiple of 256 here as well (K == 0 gives Y = +0). */
 convrot_status convrot_gemm_f16(const void* X, const void* W,
                                 int64_t M, int64_t N, int64_t K, void* Y, void* stream);
 

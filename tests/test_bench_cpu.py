@@ -75,3 +75,11 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "single-GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_host_cpu_description():
+    h = bench.host_cpu()
+    assert h["logical_cpus"] >= 1 and h["cpus_usable_by_this_process"] >= 1
+    if h["physical_cores"]:
+        assert 1 <= h["physical_cores"] <= h["logical_cpus"]
+        assert h["smt_per_core"] >= 1

@@ -7,8 +7,11 @@ Bars:
     needed.
   * W8A16 and the fp16 baseline accumulate in fp32 on the MFMA, so Y is
     compared per element against the oracle's float64 result with
-      |dY| <= ulp16(Y_ref) + 2^-14 * S_main + 2^-9 * S_lora
-    (S_* = the sums of |terms|), plus relative Frobenius error <= 1e-3.
+      |dY| <= ulp16(Y_ref) + c(K) * S_main + 2^-9 * S_lora,
+      c(K) = max(2^-14, (K + 2) 2^-24)
+    (S_* = the sums of |terms|; (K + 2) 2^-24 bounds K - 1 fp32 additions in
+    any order plus the scale multiplication, so the bound holds at every K),
+    plus relative Frobenius error <= 1e-3.
 Inputs come from workload/ (seeded) and are handed to both sides unchanged.
 """
 
@@ -544,7 +547,21 @@ def test_linear_w8a8_ex_without_extras_equals_linear_w8a8():
 
 # ------------------------------------------------ weight-only W8A16 (a6, a7)
 
-def _w8a16_case(M, N, K, rank=0, bias=False, seed=0):
+def _acc_c(K):
+    """Per-element accumulation allowance of the fp32-accumulated paths."""
+    return max(2.0 ** -14, (K + 2) * 2.0 ** -24)
+
+
+def _sample_rows(M, n=96, tile=256):
+    """Rows for oracle comparison at large M: both rows of every tile edge,
+    the first and last rows, and a seeded spread in between."""
+    edges = [r for t in range(0, M, tile) for r in (t, min(t + tile, M) - 1)]
+    rng = np.random.default_rng(M)
+    pick = rng.choice(M, min(M, n), replace=False)
+    return np.unique(np.concatenate([edges, pick, [0, M - 1]])).astype(np.int64)
+
+
+def _w8a16_case(M, N, K, rank=0, bias=False, seed=0, rows=None):
     x = wl.make_activations(M, K, seed=seed)
     w = wl.make_weights(N, K, seed=seed)
     qw, sw = O.quantize_weights(w.numpy())
@@ -556,15 +573,18 @@ def _w8a16_case(M, N, K, rank=0, bias=False, seed=0):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     yg = _np(cr.linear_w8a16(x.to(DEV), t(qw), t(sw), None if b is None else b.to(DEV),
                              None if lora is None else (lora[0].to(DEV), lora[1].to(DEV), lora[2])))
-    yo = O.linear_w8a16(x.numpy(), qw, sw, None if b is None else b.numpy(),
+    xs = x.numpy() if rows is None else x.numpy()[rows]
+    if rows is not None:
+        yg = yg[rows]
+    yo = O.linear_w8a16(xs, qw, sw, None if b is None else b.numpy(),
                         None if lora is None else (lora[0].numpy(), lora[1].numpy(), lora[2]))
-    x16r = O.rotate_activations_f16(x.numpy()).astype(np.float64)
+    x16r = O.rotate_activations_f16(xs).astype(np.float64)
     s_main = (np.abs(x16r) @ np.abs(qw.astype(np.float64)).T) * sw.astype(np.float64)[None, :]
     s_lora = 0.0
     if rank:
-        tt = np.abs(x.numpy().astype(np.float64) @ lora[0].numpy().astype(np.float64).T)
+        tt = np.abs(xs.astype(np.float64) @ lora[0].numpy().astype(np.float64).T)
         s_lora = tt @ np.abs(lora[1].numpy().astype(np.float64)).T
-    bound = _ulp16(yo) + 2.0 ** -14 * s_main + 2.0 ** -9 * s_lora
+    bound = _ulp16(yo) + _acc_c(K) * s_main + 2.0 ** -9 * s_lora
     d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
     viol = int((d > bound).sum())
     rel = float(np.linalg.norm(yg.astype(np.float64) - yo.astype(np.float64)) / np.linalg.norm(yo.astype(np.float64)))
@@ -590,19 +610,40 @@ def test_linear_w8a16_within_tolerance(M, N, K, rank, bias):
     assert viol == 0 and rel <= 1e-3
 
 
+# Shapes that select the remaining tile instances of the fp16-MFMA kernels:
+# 1024x6144x256 and 1024x8192x2048 the 256x128 tile (8 waves), 300x2048x8192
+# the 64x64 tile.  The GPU computes every row; the oracle the sampled rows,
+# which cover both edges of every 256-row tile and every column.
+TILE_SHAPES = [(1024, 6144, 256), (1024, 8192, 2048), (300, 2048, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+@pytest.mark.parametrize("rank,bias", [(0, False), (32, True)])
+def test_linear_w8a16_tile_instances(M, N, K, rank, bias):
+    _say(f"linear w8a16 tile instance M={M} N={N} K={K} rank={rank} bias={bias}")
+    viol, rel = _w8a16_case(M, N, K, rank=rank, bias=bias, seed=M + N + rank, rows=_sample_rows(M))
+    assert viol == 0 and rel <= 1e-3
+
+
 # ----------------------------------------------------------- fp16 baseline (a8)
 
-@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (300, 203, 768), (1024, 2048, 2048)])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (300, 203, 768), (1024, 2048, 2048)] + TILE_SHAPES)
 def test_gemm_f16_within_tolerance(M, N, K):
     _say(f"gemm f16 M={M} N={N} K={K}")
     x = wl.make_activations(M, K, seed=5)
     w16 = wl.make_weights(N, K, seed=5).to(torch.float16)
-    yo = O.linear_f16(x.numpy(), w16.numpy())
     yg = _np(cr.gemm_f16(x.to(DEV), w16.to(DEV)))
-    s = np.abs(x.numpy().astype(np.float64)) @ np.abs(w16.numpy().astype(np.float64)).T
-    bound = _ulp16(yo) + 2.0 ** -14 * s
+    rows = _sample_rows(M) if M * N * K > 2 ** 32 else np.arange(M)
+    xs = x.numpy()[rows]
+    yo = O.linear_f16(xs, w16.numpy())
+    yg = yg[rows]
+    s = np.abs(xs.astype(np.float64)) @ np.abs(w16.numpy().astype(np.float64)).T
+    bound = _ulp16(yo) + _acc_c(K) * s
     d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
-    assert int((d > bound).sum()) == 0
+    rel = float(np.linalg.norm(d) / np.linalg.norm(yo.astype(np.float64)))
+    _say(f"  violations {int((d > bound).sum())}, max |dY|/bound {float((d / bound).max()):.3f}, "
+         f"rel. Frobenius {rel:.2e}")
+    assert int((d > bound).sum()) == 0 and rel <= 1e-3
 
 
 # --------------------------------- dequantise-every-call baseline (next-4)
@@ -630,7 +671,7 @@ def test_dequantize_weights_bitexact_full_shapes(N, K):
 
 
 @pytest.mark.parametrize("M,N,K,bias", [(64, 256, 256, False), (300, 203, 768, True), (1024, 2048, 2048, True),
-                                        (5, 200, 4096, False)])
+                                        (5, 200, 4096, False)] + [(m, n, k, True) for (m, n, k) in TILE_SHAPES])
 def test_linear_dequant_within_tolerance(M, N, K, bias):
     _say(f"linear dequant M={M} N={N} K={K} bias={bias}")
     x = wl.make_activations(M, K, seed=M + 5)
@@ -638,10 +679,13 @@ def test_linear_dequant_within_tolerance(M, N, K, bias):
     b = wl.make_bias(N, seed=M + 5) if bias else None
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     yg = _np(cr.linear_dequant(x.to(DEV), t(qw), t(sw), None if b is None else b.to(DEV)))
-    yo = O.linear_dequant(x.numpy(), qw, sw, None if b is None else b.numpy())
+    rows = _sample_rows(M) if M * N * K > 2 ** 32 else np.arange(M)
+    xs = x.numpy()[rows]
+    yg = yg[rows]
+    yo = O.linear_dequant(xs, qw, sw, None if b is None else b.numpy())
     wd = O.dequantize_weights(qw, sw).astype(np.float64)
-    s_main = np.abs(x.numpy().astype(np.float64)) @ np.abs(wd).T
-    bound = _ulp16(yo) + 2.0 ** -14 * s_main
+    s_main = np.abs(xs.astype(np.float64)) @ np.abs(wd).T
+    bound = _ulp16(yo) + _acc_c(K) * s_main
     d = np.abs(yg.astype(np.float64) - yo.astype(np.float64))
     viol = int((d > bound).sum())
     rel = float(np.linalg.norm(d) / np.linalg.norm(yo.astype(np.float64)))
@@ -725,7 +769,15 @@ def _ulp_out(y, out):
                                                        (1024, 2048, 2048, "bf16", "bf16", True, False, "normal"),
                                                        (37, 80, 512, "f16", "bf16", False, True, "nearmax"),
                                                        (16, 256, 4096, "f16", "f16", True, True, "normal"),
-                                                       (8, 128, 1024, "bf16", "bf16", False, False, "huge")])
+                                                       (8, 128, 1024, "bf16", "bf16", False, False, "huge"),
+                                                       # K beyond fp16's largest finite value (65504)
+                                                       (4, 64, 65792, "f16", "f16", True, False, "normal"),
+                                                       (4, 64, 65792, "bf16", "bf16", False, True, "nearmax"),
+                                                       # the 256x128 and 64x64 tile instances
+                                                       (1024, 6144, 256, "f16", "f16", True, True, "normal"),
+                                                       (1024, 8192, 2048, "bf16", "bf16", False, False, "normal"),
+                                                       (1024, 8192, 2048, "f16", "bf16", True, False, "nearmax"),
+                                                       (300, 2048, 8192, "bf16", "f16", True, True, "normal")])
 def test_linear_w8a16_rs_within_tolerance(M, N, K, xd, yd, bias, res, kind):
     _say(f"range-safe w8a16 M={M} N={N} K={K} {xd}->{yd} bias={bias} residual={res} {kind}")
     x32, xt = _rs_input(M, K, xd, kind, seed=M + N)
@@ -737,19 +789,24 @@ def test_linear_w8a16_rs_within_tolerance(M, N, K, xd, yd, bias, res, kind):
     yg = cr.linear_w8a16_rs(xt.to(DEV), t(qw), t(sw), None if b is None else b.to(DEV),
                             None if r is None else r.to(DEV), out_dtype=ydt)
     yg = yg.float().cpu().numpy().astype(np.float64)
-    yo = O.linear_w8a16_rs(x32, qw, sw, None if b is None else b.numpy(),
-                           None if r is None else r.float().numpy(), out=yd).astype(np.float64)
-    pre = O.linear_w8a16_rs(x32, qw, sw, None if b is None else b.numpy(), None, out=yd).astype(np.float64)
-    x16s, e = O.rotate_rowscaled_f16(x32)
+    rows = _sample_rows(M, n=48) if M * N * K > 2 ** 32 else np.arange(M)
+    xs, yg = x32[rows], yg[rows]
+    rs = None if r is None else r.float().numpy()[rows]
+    yo = O.linear_w8a16_rs(xs, qw, sw, None if b is None else b.numpy(), rs, out=yd).astype(np.float64)
+    pre = O.linear_w8a16_rs(xs, qw, sw, None if b is None else b.numpy(), None, out=yd).astype(np.float64)
+    x16s, e = O.rotate_rowscaled_f16(xs)
     s_main = (np.abs(x16s.astype(np.float64)) @ np.abs(qw.astype(np.float64)).T) * \
         sw.astype(np.float64)[None, :] * np.exp2(e.astype(np.float64))[:, None]
-    tol = _ulp_out(pre, yd) + (_ulp_out(yo, yd) if res else 0.0) + 2.0 ** -14 * s_main
+    tol = _ulp_out(pre, yd) + (_ulp_out(yo, yd) if res else 0.0) + _acc_c(K) * s_main
     assert np.isfinite(yg).all() and np.isfinite(yo).all()
     d = np.abs(yg - yo)
     viol = int((d > tol).sum())
     rel = float(np.linalg.norm(d) / np.linalg.norm(yo))
     _say(f"  violations {viol}, max |dY|/tol {float((d / tol).max()):.3f}, rel. Frobenius {rel:.2e}")
-    assert viol == 0 and rel <= 1e-2
+    # Both sides round the same nearly equal value once to the output type, so
+    # they differ only where the fp32 accumulation moves it across a rounding
+    # boundary of that type: rare, whether the type is fp16 or bf16.
+    assert viol == 0 and rel <= 1e-3
 
 
 def test_graph_replays_of_every_path_match_eager():
