@@ -66,6 +66,8 @@ extern "C" {
 #define CONVROT_GROUP 256
 #define CONVROT_K_MAX 131072
 #define CONVROT_LORA_RANK_MAX 64
+/* Size of the fixed device scratch of convrot_linear_w8a8_noalloc. */
+#define CONVROT_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef enum convrot_status {
   CONVROT_OK = 0,
@@ -74,7 +76,9 @@ typedef enum convrot_status {
   CONVROT_ERR_ALIGNMENT = 3,   /* a tensor pointer not aligned to 16 bytes */
   CONVROT_ERR_DEVICE = 4,      /* current device is not gfx950 or cannot be queried */
   CONVROT_ERR_LAUNCH = 5,      /* a kernel launch reported an error */
-  CONVROT_ERR_WORKSPACE = 6    /* workspace NULL or smaller than convrot_workspace_bytes() */
+  CONVROT_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than convrot_workspace_bytes() */
+  CONVROT_ERR_TOO_LARGE = 7    /* convrot_linear_w8a8_noalloc: the problem needs more than
+                                  CONVROT_NOALLOC_SCRATCH_BYTES of scratch */
 } convrot_status;
 
 typedef enum convrot_path {
@@ -156,6 +160,24 @@ convrot_status convrot_linear_w8a8_ex(const void* X, int64_t M, int64_t K,
                                       const float* bias, const convrot_lora* lora,
                                       const void* residual, void* Y,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* The W8A8 linear of convrot_linear_w8a8 without a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * arithmetic, checks and bits as convrot_linear_w8a8 (workspace aside); the
+ * caller still passes X, Q_W, s_W, the optional bias and Y.  Q_X, s_X and
+ * any int32 K-split partials go to a fixed device array of
+ * CONVROT_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds per GPU from
+ * its load until the process ends, so this call allocates nothing.  A problem
+ * whose convrot_workspace_bytes(CONVROT_PATH_W8A8, M, N, K, 0) exceeds that
+ * size returns CONVROT_ERR_TOO_LARGE with nothing enqueued (e.g. M = 1024 at
+ * any K <= 16384 fits; M * K of more than about 32 Mi does not).  Every call
+ * on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (on different streams, or from several threads without ordering) race and
+ * give undefined results; order them on one stream or with events. */
+convrot_status convrot_linear_w8a8_noalloc(const void* X, int64_t M, int64_t K,
+                                           const int8_t* Q_W, const float* s_W, int64_t N,
+                                           const float* bias, void* Y, void* stream);
 
 /* The weight-only (W8A16) ConvRot linear: the weight-only listing of "What
  * changed in the computation" (x_rot fp16 [M,K], qweight int8 [N,K], one

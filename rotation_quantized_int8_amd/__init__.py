@@ -7,7 +7,7 @@ There is no CPU fallback: if the library is missing or the device is not
 gfx950, the calls raise.
 
 Functions mirror the C entry points:
-  quantize_weights, linear_w8a8, linear_w8a8_ex, linear_w8a16, linear_w8a16_rs,
+  quantize_weights, linear_w8a8, linear_w8a8_noalloc, linear_w8a8_ex, linear_w8a16, linear_w8a16_rs,
   linear_dequant, dequantize_weights, act_quant, act_rotate_f16, act_rotate_scaled,
   gemm_i8_i32, gemm_i8_f16, gemm_f16, workspace_bytes.
 """
@@ -48,6 +48,7 @@ _SIGNATURES = {
     "convrot_workspace_bytes": (_sz, [ctypes.c_int, _i64, _i64, _i64, _i64]),
     "convrot_quantize_weights": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "convrot_linear_w8a8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "convrot_linear_w8a8_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
     "convrot_linear_w8a8_ex": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, ctypes.POINTER(_Lora),
                                               _vp, _vp, _vp, _sz, _vp]),
     "convrot_linear_w8a16": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _vp,
@@ -182,6 +183,31 @@ def linear_w8a8(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
                                          _ptr(y), _ptr(ws), nbytes, _stream(x2)),
                "convrot_linear_w8a8")
     return y.reshape(*lead, N)
+
+
+def linear_w8a8_noalloc(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor,
+                        bias: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W8A8 ConvRot linear through the allocation-free entry point (the
+    library's fixed per-GPU scratch instead of a workspace).  With ``out``
+    (fp16 [M, N], contiguous, 16-byte aligned) the call allocates nothing."""
+    x2, lead = _flatten(_prep(x, torch.float16, "x"))
+    q_w = _prep(q_w, torch.int8, "Q_W")
+    s_w = _prep(s_w, torch.float32, "s_W")
+    bias = None if bias is None else _prep(bias, torch.float32, "bias")
+    M, K = x2.shape
+    N = q_w.shape[0]
+    if q_w.shape[1] != K:
+        raise ValueError(f"Q_W has K={q_w.shape[1]}, x has K={K}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    elif out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp16 tensor [M, N]")
+    with torch.cuda.device(x.device):
+        _check(lib().convrot_linear_w8a8_noalloc(_ptr(x2), M, K, _ptr(q_w), _ptr(s_w), N, _ptr(bias),
+                                                 _ptr(out), _stream(x2)),
+               "convrot_linear_w8a8_noalloc")
+    return out.reshape(*lead, N)
 
 
 def _lora_args(lora, N: int, K: int):

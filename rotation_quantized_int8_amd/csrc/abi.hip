@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "convrot.h"
 #include "launch.hpp"
@@ -139,6 +140,9 @@ const char* convrot_status_string(int status) {
     case CONVROT_ERR_DEVICE: return "current HIP device is not gfx950 or cannot be queried";
     case CONVROT_ERR_LAUNCH: return "kernel launch failed";
     case CONVROT_ERR_WORKSPACE: return "workspace missing or too small";
+    case CONVROT_ERR_TOO_LARGE:
+      return "problem needs more scratch than the allocation-free entry point holds "
+             "(CONVROT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -532,3 +536,63 @@ convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const i
 }
 
 }  // extern "C"
+
+// ------------------------------------------------ allocation-free W8A8 call
+// For callers that cannot allocate device memory.  The W8A8 path's scratch
+// (Q_X, s_X and, with few rows, the int32 K-split partials; the same layout
+// as a caller workspace) lives in this fixed device array: every GPU the
+// library runs on holds its own copy from the code object's load until the
+// process ends.  Nothing in it has to start at zero (the prologue writes Q_X
+// and s_X, and the split GEMM every partial, before anything reads them).
+
+static __device__ __align__(256) char scratch[CONVROT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this GPU's scratch array, looked up once per device with
+// that device current.  In host code `scratch` names a host-side stand-in,
+// so only this address is ever handed to a kernel.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" convrot_status convrot_linear_w8a8_noalloc(const void* X, int64_t M, int64_t K, const int8_t* Q_W,
+                                                      const float* s_W, int64_t N, const float* bias, void* Y,
+                                                      void* stream) {
+  if (M < 0 || N < 0 || K < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!k_ok(K)) return CONVROT_ERR_SHAPE;
+  if (K == 0)   // an empty contraction uses no scratch
+    return linear_w8a8_impl(X, M, K, Q_W, s_W, N, bias, nullptr, nullptr, Y, nullptr, 0, stream);
+  const size_t need = convrot_workspace_bytes(CONVROT_PATH_W8A8, M, N, K, 0);
+  if (need == (size_t)-1) return CONVROT_ERR_SHAPE;
+  if (need > (size_t)CONVROT_NOALLOC_SCRATCH_BYTES) return CONVROT_ERR_TOO_LARGE;
+  // the pointer checks come before the device lookup, as in every entry point
+  if (!X || !Q_W || !s_W || !Y) return CONVROT_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Q_W) || !aligned16(s_W) || !aligned16(Y) || (bias && !aligned16(bias)))
+    return CONVROT_ERR_ALIGNMENT;
+  const size_t yb = (size_t)M * N * 2;
+  if (overlap(Y, yb, X, (size_t)M * K * 2) || overlap(Y, yb, Q_W, (size_t)N * K) ||
+      overlap(Y, yb, s_W, (size_t)N * 4) || overlap(Y, yb, bias, bias ? (size_t)N * 4 : 0))
+    return CONVROT_ERR_INVALID_ARG;
+  if (convrot_status st = check_device()) return st;
+  void* ws = scratch_for_current_device();
+  if (!ws) return CONVROT_ERR_DEVICE;
+  return linear_w8a8_impl(X, M, K, Q_W, s_W, N, bias, nullptr, nullptr, Y, ws,
+                          (size_t)CONVROT_NOALLOC_SCRATCH_BYTES, stream);
+}

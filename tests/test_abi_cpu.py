@@ -10,7 +10,7 @@ import pytest
 import rotation_quantized_int8_amd as cr
 from rotation_quantized_int8_amd import build as crbuild
 
-OK, INVALID, SHAPE, ALIGN, DEVICE, LAUNCH, WORKSPACE = range(7)
+OK, INVALID, SHAPE, ALIGN, DEVICE, LAUNCH, WORKSPACE, TOO_LARGE = range(8)
 
 
 @pytest.fixture(scope="module")
@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     declared = cr.header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(L, name), name
     assert set(declared) == set(cr._SIGNATURES)
@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert L.convrot_abi_version() == 1
-    for s in range(7):
+    for s in range(8):
         assert L.convrot_status_string(s)
     assert b"unknown" in L.convrot_status_string(99)
 
@@ -115,6 +115,31 @@ def test_linear_w8a8_argument_errors(L):
     assert f(P, 4, 256, Q, R, 8, None, P + 16, S + 4096, ws, None) == INVALID
     assert f(P, 4, 256, Q, R, 8, None, S, S, ws, None) == INVALID
     assert f(P, 4, 256, Q, R, 8, None, S, P, ws, None) == INVALID
+
+
+def test_linear_w8a8_noalloc_argument_errors(L):
+    f = L.convrot_linear_w8a8_noalloc
+    assert f(None, 0, 256, None, None, 8, None, None, None) == OK
+    assert f(None, 4, 256, None, None, 0, None, None, None) == OK
+    assert f(P, 4, 255, Q, R, 8, None, S, None) == SHAPE
+    assert f(P, -1, 256, Q, R, 8, None, S, None) == SHAPE
+    assert f(P, 4, 131072 + 256, Q, R, 8, None, S, None) == SHAPE
+    assert f(None, 4, 256, Q, R, 8, None, S, None) == INVALID
+    assert f(P, 4, 256, Q, R, 8, None, None, None) == INVALID
+    assert f(P + 2, 4, 256, Q, R, 8, None, S, None) == ALIGN
+    assert f(P, 4, 256, Q, R, 8, R + 4096 + 4, S, None) == ALIGN
+    assert f(P, 4, 256, Q, R, 8, None, P + 16, None) == INVALID
+    # the fixed scratch holds Q_X and s_X (256-byte pieces) of at most 32 MiB:
+    # 4094 rows of 8192 fill it exactly, 4095 rows do not fit
+    cap = 32 << 20
+    assert L.convrot_workspace_bytes(0, 4094, 8, 8192, 0) == cap
+    assert L.convrot_workspace_bytes(0, 4095, 8, 8192, 0) > cap
+    assert f(P, 4095, 8192, Q, R, 8, None, S, None) == TOO_LARGE
+    assert f(P, 8192, 8192, Q, R, 8, None, S, None) == TOO_LARGE
+    assert f(None, 4095, 8192, None, None, 8, None, None, None) == TOO_LARGE
+    # a size that fits passes every host check and stops at the device check
+    # (no GPU in the CPU suite)
+    assert f(P, 4094, 8192, Q, R, 8, None, S, None) in (DEVICE, OK)
 
 
 def test_linear_w8a8_ex_argument_errors(L):
