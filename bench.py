@@ -54,6 +54,10 @@ def parse():
     p.add_argument("--counter-means", nargs="+", metavar="CSV",
                    help="print the mean of every counter per dispatch of each GEMM tile configuration "
                         "and of the prologue from rocprofv3 --pmc CSVs of a --profile-kernels run, and exit")
+    p.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                   help="find the GEMM-only sweep replays (runs of 448 consecutive GEMM dispatches) in a "
+                        "rocprofv3 --kernel-trace CSV of a default bench run, write "
+                        "profiles/gemm_i8_sweep_kernel_trace.json and exit")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
                         "of a --profile-kernels run into profiles/gemm_i8_sweep_traffic.json and exit")
@@ -113,6 +117,66 @@ GEMM_SRC = os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "gemm_dma.h
 GEMM_KERNEL = "gemm_dma_kernel"
 COPY_BYTES = 256 << 20          # calibration copy: 256 MiB read + 256 MiB written
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemm_i8_sweep_traffic.json")
+
+
+TRACE_JSON = os.path.join(ROOT, "profiles", "gemm_i8_sweep_kernel_trace.json")
+
+
+def load_trace(kernel_src):
+    """Kernel-only GEMM durations from a committed rocprofv3 trace of this source."""
+    if not os.path.exists(TRACE_JSON):
+        return None
+    with open(TRACE_JSON) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec
+
+
+def summarize_trace(path, layers=448):
+    """Mean kernel duration and span per launch of the GEMM-only sweep replays:
+    maximal runs of exactly `layers` consecutive GEMM dispatches (in dispatch
+    order), as the GEMM-only graph of this benchmark produces them."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r.get("Dispatch_Id", 0) or 0), r["Kernel_Name"],
+                         int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    runs, cur = [], []
+    for row in rows:
+        if GEMM_KERNEL in row[1]:
+            cur.append(row)
+        else:
+            if cur:
+                runs.append(cur)
+            cur = []
+    if cur:
+        runs.append(cur)
+    # graph replays run back to back (one run of k x `layers` dispatches);
+    # a run of exactly `layers` is the eager call made before capture, whose
+    # span includes host launch gaps: used only when no replay is found
+    chunks = lambda rr: [rr[i:i + layers] for i in range(0, len(rr), layers)]
+    sweeps = [c for r in runs if len(r) % layers == 0 and len(r) >= 2 * layers for c in chunks(r)]
+    if not sweeps:
+        sweeps = [r for r in runs if len(r) == layers]
+    if not sweeps:
+        raise SystemExit(f"no run of {layers} consecutive GEMM dispatches in {path}")
+    kern = [e - s for r in sweeps for (_, _, s, e) in r]
+    spans = [(r[-1][3] - r[0][2]) / layers for r in sweeps]
+    rec = {
+        "kernel": GEMM_KERNEL,
+        "source_sha256_16": source_hash(GEMM_SRC),
+        "replays": len(sweeps),
+        "launches_per_replay": layers,
+        "mean_kernel_us": round(sum(kern) / len(kern) / 1e3, 3),
+        "mean_span_per_launch_us": round(sum(spans) / len(spans) / 1e3, 3),
+    }
+    with open(TRACE_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def load_traffic(kernel_src):
@@ -434,6 +498,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "single-GPU implementation: --gpus must be 1"}), flush=True)
         log("bench.py: only --gpus 1 is supported (single-GPU implementation)")
@@ -671,6 +738,7 @@ def main():
     pro_bytes = sum((3.0 * M * s["K"] + 4.0 * M) * s["layers"] for s in per_shape)
     pro_gbs = pro_bytes / (ms_pro * 1e-3) / 1e9
     traffic = load_traffic(GEMM_SRC)
+    trace = load_trace(GEMM_SRC)
     achieved = ops_step / (ms_gemm * 1e-3) / 1e12
     out = {
         "metric": "ConvRot W8A8 linear TOPS (2MNK/t) at M=1024, 6 shapes; % int8 MFMA peak",
@@ -707,7 +775,15 @@ def main():
                             "fills and write-backs, served by the memory-side cache (MALL) or HBM; null "
                             "when the GEMM source differs from the profiled one",
             "avg_launch_us": round(ms_gemm * 1e3 / n_launch, 3),
+            "avg_launch_note": "HIP events around the graph of the 448 GEMM launches (the stream they run on), "
+                               "divided by 448: kernel time plus the in-graph dispatch gap",
             "ops_per_launch_avg": ops_step / n_launch,
+            "trace_kernel_us": trace["mean_kernel_us"] if trace else None,
+            "frac_kernel_trace": (round(ops_step / n_launch / (trace["mean_kernel_us"] * 1e-6) / 1e12 /
+                                        PEAK_INT8_TOPS, 4) if trace else None),
+            "trace_note": "mean kernel-only duration of the same GEMM launches in the committed rocprofv3 "
+                          "kernel trace of this source (profiles/gemm_i8_sweep_kernel_trace.json); null when "
+                          "the GEMM source differs from the traced one",
         },
         "stages": {
             "prologue_ms_per_step": round(ms_pro, 4),

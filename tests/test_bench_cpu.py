@@ -83,3 +83,41 @@ def test_host_cpu_description():
     if h["physical_cores"]:
         assert 1 <= h["physical_cores"] <= h["logical_cpus"]
         assert h["smt_per_core"] >= 1
+
+
+def test_summarize_trace_finds_the_gemm_only_replays(tmp_path, monkeypatch):
+    # two replays of 448 GEMM launches (1 us kernels, 2 us apart), one other
+    # run of 3 GEMMs interleaved with another kernel that must be ignored
+    rows, did, t = [], 0, 0
+    def add(name, dur, gap):
+        nonlocal did, t
+        rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur})
+        did += 1
+        t += gap
+    for _ in range(2):
+        for _ in range(448):
+            add(GEMM_A, 1000, 2000)
+        add(COPY, 500, 1000)
+    for _ in range(3):
+        add(GEMM_A, 5000, 6000)
+        add(PRO, 500, 1000)
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    out = tmp_path / "trace.json"
+    monkeypatch.setattr(bench, "TRACE_JSON", str(out))
+    bench.summarize_trace(str(path))
+    rec = json.loads(out.read_text())
+    assert rec["replays"] == 2 and rec["mean_kernel_us"] == 1.0
+    # replays launched back to back form one run of 2 x 448: split, not dropped
+    rows2 = [dict(r) for r in rows if r["Kernel_Name"] == GEMM_A][:896]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows2)
+    bench.summarize_trace(str(path))
+    assert json.loads(out.read_text())["replays"] == 2
+    # span: 447 gaps of 2 us plus the last 1 us kernel, over 448 launches
+    assert abs(rec["mean_span_per_launch_us"] - (447 * 2.0 + 1.0) / 448) < 1e-3
