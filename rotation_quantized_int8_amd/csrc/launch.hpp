@@ -22,6 +22,7 @@ struct GemmArgs {
   void* out;            // [M, N] int32 or fp16; with kc: [K / kc, M, N] int32 partials
   int64_t M, N, K;
   int64_t kc;           // 0, or K per split (kI8toI32 only; a multiple of 256 dividing K)
+  int64_t group_m;      // row tiles per group of the tile order (set by the launcher)
 };
 
 template <GemmMode MODE>
