@@ -64,6 +64,17 @@ __device__ __forceinline__ float warp_max16(float v) {
   return v;
 }
 
+// The same maximum for non-negative finite floats, on their bit patterns
+// (which order like unsigned integers): integer maxima need no NaN
+// canonicalisation, and with bound_ctrl each permutation folds into the max.
+__device__ __forceinline__ uint32_t seg_max16_bits(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max64(float v) {
   v = warp_max16(v);
   v = fmaxf(v, __shfl_xor(v, 16));

@@ -146,8 +146,8 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
     }
   }
   // row maximum: within each 16-lane segment, then one LDS atomic per segment
-  amax = warp_max16(amax);
-  if (active && lane == 0) atomicMax(&rowmax[row_in_wg], __float_as_uint(amax));
+  const uint32_t amax_bits = seg_max16_bits(__float_as_uint(amax));
+  if (active && lane == 0) atomicMax(&rowmax[row_in_wg], amax_bits);
   __syncthreads();
   if (!active) return;
   // The factor 16 of the unnormalised transform stays in the values: with
@@ -208,13 +208,16 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   // Loads are issued by every lane, unconditionally, so that the compiler
   // counts them exactly and waits only for the block it is about to use:
   // lanes without a row of block b read the last row of the matrix instead
-  // (in bounds, never used).
+  // (in bounds, never used).  Addresses advance by one grid stride of rows
+  // per step; the clamp to the last row is a pointer minimum (addresses grow
+  // with the row).
   const int rclamp = row_in_wg < sp.rows_per_wg ? row_in_wg : sp.rows_per_wg - 1;
-  auto src = [&](int64_t b) {
-    int64_t r = b * sp.rows_per_wg + rclamp;
-    r = r < M ? r : M - 1;
-    return reinterpret_cast<const v4i*>(X + r * K + (int64_t)gi * kGroup + 16 * lane);
-  };
+  const int64_t lane_off = (int64_t)gi * kGroup + 16 * lane;          // elements
+  const int64_t stride = (int64_t)gridDim.x * sp.rows_per_wg * K;     // elements per step
+  const uint16_t* const x_last = X + (M - 1) * K + lane_off;
+  const uint16_t* x_next = X + ((int64_t)blockIdx.x * sp.rows_per_wg + rclamp) * K + lane_off;
+  auto src = [&](const uint16_t* p) { return reinterpret_cast<const v4i*>(p < x_last ? p : x_last); };
+  int64_t out_off = ((int64_t)blockIdx.x * sp.rows_per_wg + row_in_wg) * K + lane_off;   // current block's row
   // Block b's data (r0, r1) is parked in the segment's LDS slot first; then
   // the same registers receive the loads of block b + gridDim.x, which are in
   // flight while block b is rotated and quantised.  A block's results are
@@ -225,23 +228,24 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   uint4 pend[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
   bool pend_active = false;
   int64_t pend_row = 0;
+  int64_t pend_off = 0;   // element offset of the held row's 16 values
   float pend_s = 0.0f;   // s_X of the held row (kQuantInt8)
   int pend_e = 0;        // exponent of the held row (kRotateScaledF16)
   auto flush = [&]() {
     if (!pend_active) return;
     if constexpr (kMode == kQuantInt8) {
-      *reinterpret_cast<uint4*>(QX + pend_row * K + (int64_t)gi * kGroup + 16 * lane) = pend[0];
+      *reinterpret_cast<uint4*>(QX + pend_off) = pend[0];
       if (gi == 0 && lane == 0) sX[pend_row] = pend_s;
     } else {
-      uint4* dst = reinterpret_cast<uint4*>(X16 + pend_row * K + (int64_t)gi * kGroup + 16 * lane);
+      uint4* dst = reinterpret_cast<uint4*>(X16 + pend_off);
       dst[0] = pend[0];
       dst[1] = pend[1];
       if (kMode == kRotateScaledF16 && gi == 0 && lane == 0) rowexp[pend_row] = pend_e;
     }
   };
 
-  v4i r0 = __builtin_nontemporal_load(src(blockIdx.x));
-  v4i r1 = __builtin_nontemporal_load(src(blockIdx.x) + 1);
+  v4i r0 = __builtin_nontemporal_load(src(x_next));
+  v4i r1 = __builtin_nontemporal_load(src(x_next) + 1);
   int it = 0;
   for (int64_t b = blockIdx.x; b < blocks; b += gridDim.x, ++it) {   // uniform trip count
     const bool active = has_row(b);
@@ -251,11 +255,14 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
       st[0] = r0;
       st[1] = r1;
     }
-    r0 = __builtin_nontemporal_load(src(b + gridDim.x));
-    r1 = __builtin_nontemporal_load(src(b + gridDim.x) + 1);
+    x_next += stride;
+    r0 = __builtin_nontemporal_load(src(x_next));
+    r1 = __builtin_nontemporal_load(src(x_next) + 1);
     flush();
     pend_active = active;
     pend_row = row;
+    pend_off = out_off;
+    out_off += stride;
     double y[16];
     if (active) rotate_staged<kBF16>(slot, lane, y);
     if constexpr (kMode == kRotateF16) {
@@ -305,9 +312,9 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
           amax = fmaxf(amax, fabsf(f[i]));
         }
       }
-      amax = warp_max16(amax);
+      const uint32_t amax_bits = seg_max16_bits(__float_as_uint(amax));
       uint32_t* rm = rowmax[it % 3];
-      if (active && lane == 0) atomicMax(&rm[row_in_wg], __float_as_uint(amax));
+      if (active && lane == 0) atomicMax(&rm[row_in_wg], amax_bits);
       __syncthreads();
       if (tid < 16) rowmax[(it + 2) % 3][tid] = 0u;
       if (active) {

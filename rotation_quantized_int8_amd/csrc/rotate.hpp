@@ -110,7 +110,8 @@ __device__ __forceinline__ void rotate_group(const __half* __restrict__ src, cha
   rotate_group<false>(reinterpret_cast<const uint16_t*>(src), slot, lane, y);
 }
 
-// Exact-definition quantisation of 16 fp32 values with scale s (> 0):
+// Exact-definition quantisation of 16 fp32 values with scale s (> 0, or 0
+// for an all-zero row, whose codes are 0):
 // q = round_half_even(fp32(v / s)).  The fast path multiplies by the
 // reciprocal; when any product lies within 3e-5 of a half-integer -- closer
 // than its possible deviation from the correctly rounded quotient -- the
@@ -119,32 +120,33 @@ __device__ __forceinline__ void rotate_group(const __half* __restrict__ src, cha
 // t half to even at the units place and holds the integer, two's complement,
 // in its low mantissa bits, so the low byte of the sum's bits is the int8
 // code.  |v / s| <= 127 (1 + 2^-23) for finite inputs, so no clamp is needed.
+// With s = 0 the reciprocal is taken as 0, so every t is 0 and the codes are
+// 0 without a separate path.
 __device__ __forceinline__ uint4 quantize16(const float (&v)[16], float s) {
   constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+  const float rcp = s == 0.0f ? 0.0f : 1.0f / s;
   uint32_t b[16];
-  if (s == 0.0f) {
+  float dmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) b[i] = 0u;
-  } else {
-    const float rcp = 1.0f / s;
-    bool near_tie = false;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float t = __fmul_rn(v[i], rcp);
-      const float m = __fadd_rn(t, kMagic);
-      near_tie |= fabsf(__fsub_rn(t, __fsub_rn(m, kMagic))) > 0.49997f;
-      b[i] = __float_as_uint(m);
-    }
-    if (near_tie) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) b[i] = __float_as_uint(__fadd_rn(v[i] / s, kMagic));
-    }
+  for (int i = 0; i < 16; ++i) {
+    const float t = __fmul_rn(v[i], rcp);
+    const float m = __fadd_rn(t, kMagic);
+    dmax = fmaxf(dmax, fabsf(__fsub_rn(t, __fsub_rn(m, kMagic))));
+    b[i] = __float_as_uint(m);
   }
+  if (dmax > 0.49997f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b[i] = __float_as_uint(__fadd_rn(v[i] / s, kMagic));
+  }
+  // low bytes of four words -> one word: bytes (b0, b1) and (b2, b3) by byte
+  // permutes, then the two halves side by side
   uint32_t w[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    w[j] = (b[4 * j] & 0xffu) | ((b[4 * j + 1] & 0xffu) << 8) | ((b[4 * j + 2] & 0xffu) << 16) |
-           (b[4 * j + 3] << 24);
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = __builtin_amdgcn_perm(b[4 * j + 1], b[4 * j], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b[4 * j + 3], b[4 * j + 2], 0x0c0c0400u);
+    w[j] = lo | (hi << 16);
+  }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 

@@ -156,7 +156,7 @@ skinny_kernel(GemmArgs p, const __half* __restrict__ Xf, int64_t kr, int rpb, in
             f[t][i] = (float)y[i];   // fp32(16 X_rot): the single rounding
             amax = fmaxf(amax, fabsf(f[t][i]));
           }
-          amax = warp_max16(amax);
+          amax = __uint_as_float(seg_max16_bits(__float_as_uint(amax)));
           if (l16 == 0) jmax[j] = amax;
         }
       }
