@@ -208,15 +208,15 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   // Loads are issued by every lane, unconditionally, so that the compiler
   // counts them exactly and waits only for the block it is about to use:
   // lanes without a row of block b read the last row of the matrix instead
-  // (in bounds, never used).  Addresses advance by one grid stride of rows
-  // per step; the clamp to the last row is a pointer minimum (addresses grow
-  // with the row).
+  // (in bounds, never used).  Element offsets advance by one grid stride of
+  // rows per step; the clamp to the last row is a minimum of offsets (they
+  // grow with the row), taken before the offset becomes an address.
   const int rclamp = row_in_wg < sp.rows_per_wg ? row_in_wg : sp.rows_per_wg - 1;
   const int64_t lane_off = (int64_t)gi * kGroup + 16 * lane;          // elements
   const int64_t stride = (int64_t)gridDim.x * sp.rows_per_wg * K;     // elements per step
-  const uint16_t* const x_last = X + (M - 1) * K + lane_off;
-  const uint16_t* x_next = X + ((int64_t)blockIdx.x * sp.rows_per_wg + rclamp) * K + lane_off;
-  auto src = [&](const uint16_t* p) { return reinterpret_cast<const v4i*>(p < x_last ? p : x_last); };
+  const int64_t x_last = (M - 1) * K + lane_off;
+  int64_t x_next = ((int64_t)blockIdx.x * sp.rows_per_wg + rclamp) * K + lane_off;
+  auto src = [&](int64_t off) { return reinterpret_cast<const v4i*>(X + (off < x_last ? off : x_last)); };
   int64_t out_off = ((int64_t)blockIdx.x * sp.rows_per_wg + row_in_wg) * K + lane_off;   // current block's row
   // Block b's data (r0, r1) is parked in the segment's LDS slot first; then
   // the same registers receive the loads of block b + gridDim.x, which are in
