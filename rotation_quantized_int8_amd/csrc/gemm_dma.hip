@@ -9,15 +9,16 @@
 //
 // Data flow (gfx950).  A workgroup of WAVES_M x WAVES_N wavefronts owns a
 // (16 FM WAVES_M) x (16 FN WAVES_N) output tile; each wavefront an FM x FN
-// block of 16x16 MFMA fragments.  K advances in slices of 128 activation
-// bytes per row (128 int8 or 64 fp16 values) through a ring of STAGES LDS
+// block of 16x16 MFMA fragments.  K advances in slices of XS = 128 or 256
+// activation bytes per row (int8 values, or half as many fp16) through a ring
+// of STAGES LDS
 // buffers filled by direct global->LDS loads (global_load_lds_dwordx4:
 // 64 lanes x 16 B = one 1 KiB block per instruction, no register staging).
 // STAGES-1 slices are in flight while one is consumed.  The ring holds the
 // activation rows of every stage first, then the weight rows of every stage,
 // and each wave loads the same number of activation blocks and of weight
-// blocks per slice.  128-byte LDS rows
-// have their 16-byte chunks XOR-swizzled by (row & 7); the weight-only
+// blocks per slice.  256- and 128-byte LDS rows have their 16-byte chunks
+// XOR-swizzled by (row & 15) and (row & 7); the weight-only
 // mode's int8 weight rows are 64 bytes per slice (16 rows per block) with
 // their chunks swizzled by ((row >> 2) & 3).  Both make the fills and the
 // fragment reads conflict-free; a direct load places a lane's chunk at its
