@@ -250,11 +250,7 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   for (int64_t b = blockIdx.x; b < blocks; b += gridDim.x, ++it) {   // uniform trip count
     const bool active = has_row(b);
     const int64_t row = b * sp.rows_per_wg + row_in_wg;
-    if (active) {
-      v4i* st = reinterpret_cast<v4i*>(slot + 32 * lane);
-      st[0] = r0;
-      st[1] = r1;
-    }
+    if (active) park_row(slot, lane, r0, r1);
     x_next += stride;
     r0 = __builtin_nontemporal_load(src(x_next));
     r1 = __builtin_nontemporal_load(src(x_next) + 1);

@@ -18,7 +18,10 @@
 // and H = H16 (x) H16 (up to the 1/16), so the transform is a 16-point
 // transform along a followed by one along b.  Each group is owned by 16
 // consecutive lanes of one wavefront (a "segment") and a private LDS slot:
-//   1. lane a holds row a (32 contiguous bytes) and parks it in the slot;
+//   1. lane a holds row a (32 contiguous bytes) and parks its two 16-byte
+//      halves in two regions of the slot (the first halves of the 16 rows,
+//      then the second halves: each parking store covers all banks once,
+//      where 32-byte rows put lanes a and a + 8 on the same banks);
 //   2. lane b reads column b back, transforms along a in registers (fp64);
 //   3. the columns go through an XOR-swizzled fp64 transpose in the slot;
 //   4. lane c holds row c, transforms along b in registers -> 16 contiguous
@@ -31,6 +34,14 @@
 namespace convrot {
 
 constexpr int kSlotBytes = 2048 + 64;  // one group: 256 doubles + bank-offset pad
+constexpr int kParkHi = 272;           // byte offset of the second-half region (256 + a 16-byte bank offset)
+
+// Step 1: row `lane` of the group, as its halves r0 (elements 16 lane .. +7)
+// and r1 (+8 .. +15), into the slot's two parking regions.
+__device__ __forceinline__ void park_row(char* slot, int lane, v4i r0, v4i r1) {
+  *reinterpret_cast<v4i*>(slot + 16 * lane) = r0;
+  *reinterpret_cast<v4i*>(slot + kParkHi + 16 * lane) = r1;
+}
 
 __device__ __forceinline__ void fwht16(double (&v)[16]) {
 #pragma unroll
@@ -54,8 +65,7 @@ __device__ __forceinline__ double in16_to_f64(uint16_t bits) {
 }
 
 // Steps 2-4 for a group of 16-bit values (fp16, or bf16 with kBF16) already
-// staged in `slot` (row a of the 16x16 view, 32 bytes, at byte 32 a; written
-// by lanes of this wavefront).  On return y[] holds 16 * x_rot of row `lane`
+// parked in `slot` by park_row (written by lanes of this wavefront).  On return y[] holds 16 * x_rot of row `lane`
 // of the group: exact for fp16 inputs, and for bf16 inputs whenever the
 // group's values span at most 45 binades (every partial sum then fits 53
 // bits).  `slot` is the segment's private LDS slot (kSlotBytes); it is free
@@ -63,11 +73,11 @@ __device__ __forceinline__ double in16_to_f64(uint16_t bits) {
 template <bool kBF16 = false>
 __device__ __forceinline__ void rotate_staged(char* slot, int lane, double (&y)[16]) {
   wave_lds_sync();
-  // column `lane`: element (a, lane) for a = 0..15
-  const uint16_t* sh = reinterpret_cast<const uint16_t*>(slot);
+  // column `lane`: element (a, lane) for a = 0..15, from its column's half region
+  const uint16_t* sh = reinterpret_cast<const uint16_t*>(slot + (lane < 8 ? 0 : kParkHi));
   double v[16];
 #pragma unroll
-  for (int a = 0; a < 16; ++a) v[a] = in16_to_f64<kBF16>(sh[16 * a + lane]);
+  for (int a = 0; a < 16; ++a) v[a] = in16_to_f64<kBF16>(sh[8 * a + (lane & 7)]);
   wave_lds_sync();  // all staging reads done before the slot is reused below
   fwht16(v);        // along a: v[c] = Z[c][lane]
   // transpose: Z[c][b] at row c, 16-byte chunk (b >> 1) ^ (c & 7)
@@ -90,9 +100,7 @@ __device__ __forceinline__ void rotate_staged(char* slot, int lane, double (&y)[
 // of the group as two 16-byte halves r0, r1 and parks it in the slot first.
 template <bool kBF16 = false>
 __device__ __forceinline__ void rotate_loaded(v4i r0, v4i r1, char* slot, int lane, double (&y)[16]) {
-  v4i* st = reinterpret_cast<v4i*>(slot + 32 * lane);
-  st[0] = r0;
-  st[1] = r1;
+  park_row(slot, lane, r0, r1);
   rotate_staged<kBF16>(slot, lane, y);
 }
 
