@@ -108,13 +108,18 @@ def capture(fn, stream):
     return g
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(*paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 GEMM_SRC = os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "gemm_dma.hip")
 GEMM_KERNEL = "gemm_dma_kernel"
+PROLOGUE_SRC = (os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "prologue.hip"),
+                os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "rotate.hpp"))
 COPY_BYTES = 256 << 20          # calibration copy: 256 MiB read + 256 MiB written
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemm_i8_sweep_traffic.json")
 
@@ -179,6 +184,18 @@ def summarize_trace(path, layers=448):
     print(json.dumps(rec))
 
 
+def load_prologue_hbm_traffic():
+    """Measured L2 fill + write-back bytes of the HBM-scale prologue call,
+    valid only for the prologue sources it was taken on."""
+    if not os.path.exists(TRAFFIC_JSON):
+        return None
+    with open(TRAFFIC_JSON) as f:
+        rec = json.load(f).get("prologue_hbm_scale")
+    if not rec or rec.get("source_sha256_16") != source_hash(*PROLOGUE_SRC):
+        return None
+    return rec
+
+
 def load_traffic(kernel_src):
     """Measured HBM bytes per launch of the GEMM, valid only for this source."""
     path = TRAFFIC_JSON
@@ -192,36 +209,50 @@ def load_traffic(kernel_src):
 
 
 def _pmc_rows(path, counter):
-    """(kernel name, value in KiB) per dispatch of one counter from rocprofv3's CSV."""
+    """(dispatch id, kernel name, value) per dispatch of one counter from
+    rocprofv3's CSV, in dispatch order."""
     import csv
     rows = []
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
             if r.get("Counter_Name") == counter:
-                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort(key=lambda r: r[0])
     return rows
+
+
+def _copy_dispatch(rows):
+    """Dispatch id of the calibration copy of a --profile-kernels run (the
+    bitwise-not elementwise kernel), or None.  Prologue dispatches after it
+    are the HBM-scale call."""
+    ids = [i for (i, k, _) in rows if "bitwise_not" in k]
+    return ids[-1] if ids else None
 
 
 def counter_means(paths):
     """Mean of each counter per dispatch, per GEMM instance (its template
-    arguments) and for the prologue, over rocprofv3 --pmc CSV files."""
+    arguments), for the sweep's prologue launches and for the HBM-scale
+    prologue call after the calibration copy, over rocprofv3 --pmc CSV files."""
     import csv
     import collections
     sums = collections.defaultdict(lambda: collections.defaultdict(float))
     count = collections.defaultdict(collections.Counter)
     for path in paths:
         with open(path, newline="") as f:
-            for r in csv.DictReader(f):
-                k = r["Kernel_Name"]
-                if GEMM_KERNEL in k:
-                    m = re.search(r"gemm_dma_kernel<([^>]*)>", k)
-                    key = "gemm<" + (m.group(1) if m else "?") + ">"
-                elif "prologue_" in k:
-                    key = "prologue"
-                else:
-                    continue
-                sums[key][r["Counter_Name"]] += float(r["Counter_Value"])
-                count[key][r["Counter_Name"]] += 1
+            rows = list(csv.DictReader(f))
+        copy_ids = [int(r["Dispatch_Id"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
+        copy_id = max(copy_ids) if copy_ids else None
+        for r in rows:
+            k = r["Kernel_Name"]
+            if GEMM_KERNEL in k:
+                m = re.search(r"gemm_dma_kernel<([^>]*)>", k)
+                key = "gemm<" + (m.group(1) if m else "?") + ">"
+            elif "prologue_" in k:
+                key = "prologue" if copy_id is None or int(r["Dispatch_Id"]) < copy_id else "prologue_hbm_scale"
+            else:
+                continue
+            sums[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            count[key][r["Counter_Name"]] += 1
     out = {key: {"dispatches": max(count[key].values()),
                  **{c: round(v / count[key][c], 1) for c, v in sorted(cs.items())}}
            for key, cs in sums.items()}
@@ -236,14 +267,15 @@ def summarize_pmc(fetch_csv, write_csv):
 
     def calib(rows, what):
         # the copy is the largest elementwise dispatch of the profiling run
-        cands = [v for (k, v) in rows if "elementwise" in k.lower() or "copy" in k.lower()]
+        cands = [v for (_, k, v) in rows if "elementwise" in k.lower() or "copy" in k.lower()]
         if not cands:
             raise SystemExit(f"no calibration copy found for {what}")
         return COPY_BYTES / (max(cands) * 1024.0)
 
     fr, wr = calib(fetch, "FETCH_SIZE"), calib(write, "WRITE_SIZE")
-    gf = [v for (k, v) in fetch if GEMM_KERNEL in k]
-    gw = [v for (k, v) in write if GEMM_KERNEL in k]
+    cf, cw = _copy_dispatch(fetch), _copy_dispatch(write)
+    gf = [v for (_, k, v) in fetch if GEMM_KERNEL in k]
+    gw = [v for (_, k, v) in write if GEMM_KERNEL in k]
     if not gf or len(gf) != len(gw):
         raise SystemExit("GEMM dispatch counts differ between the two runs")
     per_launch = (sum(gf) * fr + sum(gw) * wr) * 1024.0 / len(gf)
@@ -256,9 +288,12 @@ def summarize_pmc(fetch_csv, write_csv):
         "copy_calibration": {"bytes": COPY_BYTES, "fetch_factor": round(fr, 4), "write_factor": round(wr, 4)},
         "hbm_bytes_per_launch": round(per_launch),
     }
-    # the activation prologue of the same run (not the roofline kernel)
-    pf = [v for (k, v) in fetch if "prologue_" in k]
-    pw = [v for (k, v) in write if "prologue_" in k]
+    # the activation prologue of the same run (not the roofline kernel): the
+    # sweep's launches, then the one HBM-scale call after the calibration copy
+    pf = [v for (i, k, v) in fetch if "prologue_" in k and (cf is None or i < cf)]
+    pw = [v for (i, k, v) in write if "prologue_" in k and (cw is None or i < cw)]
+    hf = [v for (i, k, v) in fetch if "prologue_" in k and cf is not None and i > cf]
+    hw = [v for (i, k, v) in write if "prologue_" in k and cw is not None and i > cw]
     if pf and len(pf) == len(pw):
         import workload as wl
         layers = sum(n for (_, _, n) in wl.LAYER_SHAPES)
@@ -270,6 +305,18 @@ def summarize_pmc(fetch_csv, write_csv):
             "write_kib_per_launch_raw": round(sum(pw) / len(pw), 1),
             "hbm_bytes_per_launch": round((sum(pf) * fr + sum(pw) * wr) * 1024.0 / len(pf)),
             "algorithmic_bytes_per_launch": round(algo),
+        }
+    if hf and len(hf) == len(hw):
+        M, K = HBM_SCALE_MK
+        rec["prologue_hbm_scale"] = {
+            "kernel": "prologue_persistent_kernel",
+            "source_sha256_16": source_hash(*PROLOGUE_SRC),
+            "M": M, "K": K,
+            "launches": len(hf),
+            "fetch_kib_per_launch_raw": round(sum(hf) / len(hf), 1),
+            "write_kib_per_launch_raw": round(sum(hw) / len(hw), 1),
+            "hbm_bytes_per_launch": round((sum(hf) * fr + sum(hw) * wr) * 1024.0 / len(hf)),
+            "algorithmic_bytes_per_launch": round(3.0 * M * K + 4.0 * M),
         }
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(rec, f, indent=1)
@@ -313,11 +360,14 @@ def device_copy_gbs(torch, dev, stream):
     return round(2.0 * n / (best * 1e-3) / 1e9, 1)
 
 
+HBM_SCALE_MK = (16384, 8192)   # the prologue alone beyond the memory-side cache
+
+
 def prologue_at_hbm_scale(L, torch, wl, dev, stream):
     """The activation prologue alone at M = 16384, K = 8192: two 256 MiB fp16
     inputs used in turn (with the 128 MiB int8 output, beyond the 256 MB
     memory-side cache), 10 calls per graph; algorithmic bytes 3 M K + 4 M."""
-    M, K = 16384, 8192
+    M, K = HBM_SCALE_MK
     xs = [wl.make_activations(M, K, seed=i).to(dev) for i in range(2)]
     qx = torch.empty((M, K), dtype=torch.int8, device=dev)
     sx = torch.empty(M, dtype=torch.float32, device=dev)
@@ -594,6 +644,17 @@ def main():
         torch.cuda.synchronize()
         torch.bitwise_not(src, out=dst)      # elementwise: reads and writes COPY_BYTES
         torch.cuda.synchronize()
+        del src, dst
+        # the prologue alone at HBM scale, once, after the copy
+        hm, hk = HBM_SCALE_MK
+        hx = wl.make_activations(hm, hk, seed=1).to(dev)
+        hq = torch.empty((hm, hk), dtype=torch.int8, device=dev)
+        hs = torch.empty(hm, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        st = fpro(hx.data_ptr(), hm, hk, hq.data_ptr(), hs.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise RuntimeError(L.convrot_status_string(st).decode())
+        torch.cuda.synchronize()
         log("profile run done")
         return
 
@@ -726,6 +787,11 @@ def main():
 
         log("prologue at HBM scale (M = 16384, K = 8192) and the device copy rate")
         pro_large = prologue_at_hbm_scale(L, torch, wl, dev, stream)
+        pt = load_prologue_hbm_traffic()
+        pro_large["traffic"] = pt["hbm_bytes_per_launch"] if pt else None
+        pro_large["traffic_note"] = ("FETCH_SIZE + WRITE_SIZE of one such call (profiles/gemm_i8_sweep_traffic.json, "
+                                     "scaled by the calibration copy) against 3 M K + 4 M algorithmic bytes; null when "
+                                     "the prologue source differs from the profiled one")
         copy_gbs = device_copy_gbs(torch, dev, stream)
         pro_large["frac_of_device_copy"] = round(pro_large["gbs"] / copy_gbs, 4)
 

@@ -47,6 +47,30 @@ def test_summarize_pmc_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert rec["source_sha256_16"] == bench.source_hash(bench.GEMM_SRC)
 
 
+def test_summarize_pmc_splits_the_hbm_scale_prologue(tmp_path, monkeypatch):
+    # --profile-kernels order: the sweep (prologue + GEMM), the calibration
+    # copy (bitwise not), then one prologue call at HBM scale
+    kib = 1024.0
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::bitwise_not_kernel_cuda(x)>(z)"
+    fetch = [(PRO, 10.0), (GEMM_A, 100.0), (PRO, 12.0), (GEMM_A, 300.0), (copy, bench.COPY_BYTES / kib / 2),
+             (PRO, 5000.0)]
+    write = [(PRO, 4.0), (GEMM_A, 50.0), (PRO, 6.0), (GEMM_A, 70.0), (copy, bench.COPY_BYTES / kib), (PRO, 900.0)]
+    _write(tmp_path / "f.csv", "FETCH_SIZE", fetch)
+    _write(tmp_path / "w.csv", "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(out))
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    rec = json.loads(out.read_text())
+    assert rec["launches"] == 2
+    assert rec["prologue"]["launches"] == 2
+    assert rec["prologue"]["hbm_bytes_per_launch"] == round((11.0 * 2 + 5.0) * 1024)
+    h = rec["prologue_hbm_scale"]
+    M, K = bench.HBM_SCALE_MK
+    assert h["launches"] == 1 and (h["M"], h["K"]) == (M, K)
+    assert h["hbm_bytes_per_launch"] == round((5000.0 * 2 + 900.0) * 1024)
+    assert h["algorithmic_bytes_per_launch"] == 3 * M * K + 4 * M
+
+
 def test_summarize_pmc_rejects_mismatched_runs(tmp_path, monkeypatch):
     _write(tmp_path / "f.csv", "FETCH_SIZE", [(COPY, 1.0), (GEMM_A, 1.0), (GEMM_A, 2.0)])
     _write(tmp_path / "w.csv", "WRITE_SIZE", [(COPY, 1.0), (GEMM_A, 1.0)])
@@ -68,6 +92,15 @@ def test_counter_means_per_configuration(tmp_path, capsys):
     assert b["SQ_INSTS_MFMA"] == 4.0 and b["dispatches"] == 1
     assert out["prologue"]["SQ_WAVES"] == 16.0
     assert len(out) == 3      # the copy kernel is not reported
+
+
+def test_counter_means_keeps_the_hbm_scale_prologue_apart(tmp_path, capsys):
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::bitwise_not_kernel_cuda(x)>(z)"
+    _write(tmp_path / "a.csv", "SQ_WAVES", [(PRO, 16.0), (GEMM_A, 8.0), (PRO, 16.0), (copy, 1.0), (PRO, 512.0)])
+    bench.counter_means([str(tmp_path / "a.csv")])
+    out = json.loads(capsys.readouterr().out)
+    assert out["prologue"]["SQ_WAVES"] == 16.0 and out["prologue"]["dispatches"] == 2
+    assert out["prologue_hbm_scale"]["SQ_WAVES"] == 512.0
 
 
 def test_more_than_one_gpu_is_refused():
