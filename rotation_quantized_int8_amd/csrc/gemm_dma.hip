@@ -171,7 +171,9 @@ gemm_dma_kernel(GemmArgs p) {
   static_assert(XBLK % NW == 0 && WBLK % NW == 0, "blocks must split evenly over waves");
   static_assert(BN % WROWS == 0 && BM % XROWS == 0, "whole blocks");
   static_assert(NKK % 2 == 0, "fragment buffers alternate per K step");
-  static_assert(STAGES >= 3 && kAhead < 64, "pipeline depth");
+  // Two stages keep one slice in flight while one is consumed (the refill of
+  // a buffer still waits for the barrier after its last reads).
+  static_assert(STAGES >= 2 && kAhead < 64, "pipeline depth");
 
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x;
@@ -697,6 +699,7 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
         case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4, true>(a, stream);
         case 10: return launch_cfg<MODE, 2, 2, 2, 2, 4, true>(a, stream);
         case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3, true>(a, stream);
+        case 21: return launch_cfg<MODE, 4, 2, 4, 4, 3, true>(a, stream);   // extras: the 256x128 tile
         case 19: return launch_cfg<MODE, 2, 2, 1, 1, 4, true, 256>(a, stream);
         case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, true, 256>(a, stream);
         default: return hipErrorInvalidValue;
@@ -710,6 +713,10 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 9: return launch_cfg<MODE, 2, 2, 1, 2, 4>(a, stream);   // 32x64
     case 10: return launch_cfg<MODE, 2, 2, 2, 2, 4>(a, stream);  // 64x64
     case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3>(a, stream);  // 256x128, 8 waves of 64x64
+    case 21:   // 128x128, 4 waves of 64x64, 2 stages (64 KiB: two workgroups per CU), fp16 output
+      if constexpr (MODE == GemmMode::kI8toF16)
+        return launch_cfg<MODE, 2, 2, 4, 4, 2>(a, stream);
+      return hipErrorInvalidValue;
     case 19: return launch_cfg<MODE, 2, 2, 1, 1, 4, false, 256>(a, stream);  // 32x32, 256-byte K slices
     case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, false, 256>(a, stream);  // 128x64, 8 waves of 32x32, 256-byte K slices
     default: return hipErrorInvalidValue;

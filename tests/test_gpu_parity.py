@@ -205,7 +205,8 @@ def test_gemm_i8_f16_bitexact_given_same_inputs(M, N, K, with_bias):
 
 def test_gemm_i8_f16_repeated_launches_every_tile():
     """Back-to-back launches over shapes that select each int8 tile
-    configuration (256x128, 128x64, 64x64 and 32x32 tiles), interleaved so
+    configuration (128x128 on two stages, 256x128, 128x64, 64x64 and 32x32
+    tiles), interleaved so
     that the timing of one launch differs from the next; every output must
     equal the oracle bit for bit.  Guards the ordering of the LDS writes of
     the staged output tile before the barrier that publishes them."""
