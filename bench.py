@@ -64,11 +64,18 @@ def parse():
     return p.parse_args()
 
 
+SPIN_CYCLES = 2_000_000   # about 1 ms of GPU clock cycles
+
+
 def timed_graph(graph, steps, warmup, stream):
+    """ms per replay over `steps` back-to-back replays after `warmup` ones,
+    the first timed replay queued behind a short GPU spin (see median_sets)."""
     import torch
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -80,7 +87,10 @@ def timed_graph(graph, steps, warmup, stream):
 
 
 def median_sets(graph, sets, stream):
-    """Median over `sets` individually timed replays (ms per replay)."""
+    """Median over `sets` individually timed replays (ms per replay).  Each
+    timed replay is queued behind a short GPU spin, so that neither the
+    host's graph submission nor the clock ramp-up after the idle
+    synchronisation between sets falls inside the timed region."""
     import torch
     graph.replay()
     torch.cuda.synchronize()
@@ -88,6 +98,8 @@ def median_sets(graph, sets, stream):
     for _ in range(sets):
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(SPIN_CYCLES)
         start.record(stream)
         graph.replay()
         end.record(stream)
