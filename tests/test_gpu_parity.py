@@ -694,6 +694,69 @@ def test_linear_dequant_within_tolerance(M, N, K, bias):
     assert viol == 0 and rel <= 1e-3
 
 
+# ------------------------------------- one-launch layer for K = 256 (next-1)
+# With K = 256 each row is a single rotation group, so for 16 < M <= 2048 and
+# N a multiple of 4 the layer runs as one launch in which every workgroup
+# quantises its band of 32 rows itself.  Cases cover a single ragged band,
+# ragged 64-column chunks, rows that are not 16-byte aligned (N % 8 = 4),
+# fewer chunks than wavefronts, and the wide column groups whose wavefronts
+# loop over several chunks (M = 1500, 2048 and N = 12288 at M = 1024).
+
+@pytest.mark.parametrize("M,N,bias,dist", [(17, 4, False, "normal"), (31, 60, True, "t3"),
+                                           (32, 64, False, "normal"), (33, 100, True, "normal"),
+                                           (100, 252, False, "t3"), (513, 2048, True, "normal"),
+                                           (1000, 6148, False, "t3"), (1500, 6144, True, "normal"),
+                                           (2048, 4096, False, "normal"), (1024, 12288, True, "t3")])
+def test_linear_w8a8_band_bitexact(M, N, bias, dist):
+    _say(f"linear w8a8 one launch K=256 M={M} N={N} bias={bias} {dist}")
+    rows = None
+    if M * N > (1 << 21):
+        rows = np.unique(np.concatenate([np.random.default_rng(M + N).choice(M, 96, replace=False),
+                                         [0, 31, 32, M - 1]]))
+    mism, emax, rel = _w8a8_case(M, N, 256, seed=M * 3 + N, dist=dist, bias=bias, rows=rows)
+    assert mism == 0 and emax == 0.0
+
+
+def test_linear_w8a8_band_special_rows():
+    # rounding-tie rows (their first group, whose maximum decides the row
+    # scale), a zero row, fp16 extremes, subnormals and a constant row,
+    # filling a ragged second band
+    _say("linear w8a8 one launch K=256 special rows")
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+    rows = []
+    for r in g["tie_rows"]["rows"]:
+        x = np.empty(256)
+        x[0:256:2] = r["x_even_num"] / r["den"]
+        x[1:256:2] = r["x_odd_num"] / r["den"]
+        rows.append(x)
+    rows.append(np.zeros(256))
+    rows.append(np.full(256, 65504.0))
+    rows.append(np.full(256, -65504.0))
+    rows.append(np.where(np.arange(256) % 3 == 0, 2.0 ** -24, -(2.0 ** -24)))
+    rows.append(np.full(256, 0.5))
+    rest = wl.make_activations(40 - len(rows), 256, seed=77).numpy().astype(np.float64)
+    x = np.concatenate([np.array(rows), rest]).astype(np.float16)
+    w = wl.make_weights(72, 256, seed=78)
+    qw, sw = O.quantize_weights(w.numpy())
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    yg = _np(cr.linear_w8a8(t(x), t(qw), t(sw)))
+    with np.errstate(over="ignore"):   # the fp16-max rows overflow Y to +-inf on both sides
+        yo, qx, sx, a = O.linear_w8a8(x, qw, sw, None)
+    assert list(qx[:4, 1]) == [r["Q_X_1"] for r in g["tie_rows"]["rows"]]
+    assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+    assert not yg[4].any()
+
+
+@pytest.mark.parametrize("M,N", [(33, 100), (100, 252), (1024, 6144), (1500, 6144)])
+def test_linear_w8a8_band_residual_in_place(M, N):
+    # bias and an fp16 residual that is the output buffer itself
+    _say(f"linear w8a8_ex one launch K=256 in place M={M} N={N}")
+    yg, yo, tol = _w8a8_ex_case(M, N, 256, seed=M + N, bias=True, in_place=True)
+    assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+
+
 # ------------------------------------------ few activation rows (next-1)
 # M <= 16 with M K <= 8192 runs as one fused launch; M <= 16 with N <= 4096
 # otherwise runs the prologue and the few-row kernel (K split into int32
