@@ -49,7 +49,7 @@ def parse():
     p.add_argument("--no-compare", action="store_true", help="skip the W8A16 / fp16 comparison sweeps")
     p.add_argument("--no-m-sweep", action="store_true", help="skip the row-count sweep on the two large shapes")
     p.add_argument("--profile-kernels", action="store_true",
-                   help="run one eager W8A8 step plus a calibration copy of known size and exit "
+                   help="run the sweep as prologue + GEMM per layer (twice) plus a calibration copy of known size and exit "
                         "(the program to run under rocprofv3 --pmc)")
     p.add_argument("--counter-means", nargs="+", metavar="CSV",
                    help="print the mean of every counter per dispatch of each GEMM tile configuration "
@@ -129,6 +129,8 @@ def source_hash(*paths):
 
 
 GEMM_SRC = os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "gemm_dma.hip")
+BAND_SRC = os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "band.hip")
+BAND_KERNEL = "band_kernel"
 GEMM_KERNEL = "gemm_dma_kernel"
 PROLOGUE_SRC = (os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "prologue.hip"),
                 os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc", "rotate.hpp"))
@@ -261,6 +263,8 @@ def counter_means(paths):
                 key = "gemm<" + (m.group(1) if m else "?") + ">"
             elif "prologue_" in k:
                 key = "prologue" if copy_id is None or int(r["Dispatch_Id"]) < copy_id else "prologue_hbm_scale"
+            elif BAND_KERNEL in k:
+                key = "band"
             else:
                 continue
             sums[key][r["Counter_Name"]] += float(r["Counter_Value"])
@@ -317,6 +321,25 @@ def summarize_pmc(fetch_csv, write_csv):
             "write_kib_per_launch_raw": round(sum(pw) / len(pw), 1),
             "hbm_bytes_per_launch": round((sum(pf) * fr + sum(pw) * wr) * 1024.0 / len(pf)),
             "algorithmic_bytes_per_launch": round(algo),
+        }
+    # the one-launch K = 256 layer of the same run
+    bf = [v for (_, k, v) in fetch if BAND_KERNEL in k]
+    bw = [v for (_, k, v) in write if BAND_KERNEL in k]
+    if bf and len(bf) == len(bw):
+        import workload as wl
+        M = wl.M_FIXED
+        shapes = [(n, k) for (n, k, _) in wl.LAYER_SHAPES if k == 256]
+        n, k = shapes[0]
+        rec["band"] = {
+            "kernel": BAND_KERNEL,
+            "source_sha256_16": source_hash(BAND_SRC),
+            "M": M, "N": n, "K": k,
+            "launches": len(bf),
+            "fetch_kib_per_launch_raw": round(sum(bf) / len(bf), 1),
+            "write_kib_per_launch_raw": round(sum(bw) / len(bw), 1),
+            "hbm_bytes_per_launch": round((sum(bf) * fr + sum(bw) * wr) * 1024.0 / len(bf)),
+            # X fp16 once, Q_W and s_W once, Y fp16 once
+            "algorithmic_bytes_per_launch": round(2.0 * M * k + n * k + 4.0 * n + 2.0 * M * n),
         }
     if hf and len(hf) == len(hw):
         M, K = HBM_SCALE_MK
@@ -646,11 +669,39 @@ def main():
                 if st:
                     raise RuntimeError(L.convrot_status_string(st).decode())
 
+    def staged_step():
+        # every layer as the prologue and the GEMM, each GEMM reading the Q_X
+        # its prologue has just written (the W8A8 step itself runs the K = 256
+        # layers as one launch instead)
+        h = torch.cuda.current_stream().cuda_stream
+        for s in per_shape:
+            for q in s["qws"]:
+                st = fpro(s["x"].data_ptr(), M, s["K"], s["qx"].data_ptr(), s["sx"].data_ptr(), h)
+                if st == 0:
+                    st = fgemm(s["qx"].data_ptr(), s["sx"].data_ptr(), q.data_ptr(), s["sw"].data_ptr(), None,
+                               M, s["N"], s["K"], s["y"].data_ptr(), h)
+                if st:
+                    raise RuntimeError(L.convrot_status_string(st).decode())
+
+    def band_layers():
+        # the layers the W8A8 step runs as one launch (K = 256), that way
+        h = torch.cuda.current_stream().cuda_stream
+        for s in per_shape:
+            if s["K"] != 256:
+                continue
+            for q in s["qws"]:
+                st = f8a8(s["x"].data_ptr(), M, s["K"], q.data_ptr(), s["sw"].data_ptr(), s["N"], None,
+                          s["y"].data_ptr(), s["ws8"].data_ptr(), s["ws8"].numel(), h)
+                if st:
+                    raise RuntimeError(L.convrot_status_string(st).decode())
+
     if args.profile_kernels:
-        log("profile run: one eager W8A8 step, then the calibration copy")
-        w8a8_step()
-        torch.cuda.synchronize()
-        w8a8_step()
+        log("profile run: the sweep as prologue + GEMM per layer and the one-launch K = 256 layers, "
+            "twice, then the calibration copy")
+        for _ in range(2):
+            staged_step()
+            band_layers()
+            torch.cuda.synchronize()
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()

@@ -71,6 +71,37 @@ def test_summarize_pmc_splits_the_hbm_scale_prologue(tmp_path, monkeypatch):
     assert h["algorithmic_bytes_per_launch"] == 3 * M * K + 4 * M
 
 
+BAND = "void convrot::(anonymous namespace)::band_kernel<32>(convrot::GemmArgs, __half const*, long, long)"
+
+
+def test_summarize_pmc_reports_the_one_launch_layer(tmp_path, monkeypatch):
+    # the K = 256 layers run as one launch after the staged sweep; their
+    # traffic is its own record, not part of the GEMM's average
+    kib = 1024.0
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::bitwise_not_kernel_cuda(x)>(z)"
+    fetch = [(PRO, 10.0), (GEMM_A, 100.0), (BAND, 3000.0), (BAND, 3100.0), (copy, bench.COPY_BYTES / kib / 2)]
+    write = [(PRO, 4.0), (GEMM_A, 50.0), (BAND, 12000.0), (BAND, 12000.0), (copy, bench.COPY_BYTES / kib)]
+    _write(tmp_path / "f.csv", "FETCH_SIZE", fetch)
+    _write(tmp_path / "w.csv", "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(out))
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    rec = json.loads(out.read_text())
+    assert rec["launches"] == 1 and rec["hbm_bytes_per_launch"] == round((100.0 * 2 + 50.0) * 1024)
+    b = rec["band"]
+    assert b["launches"] == 2 and b["K"] == 256
+    assert b["hbm_bytes_per_launch"] == round((3050.0 * 2 + 12000.0) * 1024)
+    M, N = b["M"], b["N"]
+    assert b["algorithmic_bytes_per_launch"] == 2 * M * 256 + N * 256 + 4 * N + 2 * M * N
+
+
+def test_counter_means_reports_the_one_launch_layer(tmp_path, capsys):
+    _write(tmp_path / "a.csv", "SQ_INSTS_VALU", [(GEMM_A, 10.0), (BAND, 500.0), (BAND, 700.0)])
+    bench.counter_means([str(tmp_path / "a.csv")])
+    out = json.loads(capsys.readouterr().out)
+    assert out["band"]["SQ_INSTS_VALU"] == 600.0 and out["band"]["dispatches"] == 2
+
+
 def test_summarize_pmc_rejects_mismatched_runs(tmp_path, monkeypatch):
     _write(tmp_path / "f.csv", "FETCH_SIZE", [(COPY, 1.0), (GEMM_A, 1.0), (GEMM_A, 2.0)])
     _write(tmp_path / "w.csv", "WRITE_SIZE", [(COPY, 1.0), (GEMM_A, 1.0)])
