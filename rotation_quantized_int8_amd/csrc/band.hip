@@ -138,7 +138,7 @@ __device__ __forceinline__ v4i add_f16x8(v4i a, v4i b) {
 }
 
 // groups: column groups; tpg: 128-column tiles per group.
-template <int BR>
+template <int BR, bool kBias>
 __global__ void __launch_bounds__(64 * kWaves)
 band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
   using L = BandLayout<BR>;
@@ -161,24 +161,27 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
   // chunk (l % 16) ^ (row & 15)), and for wavefront 0 the scale block (lanes
   // 0-31: s_W of the tile's columns in quads, 32-63: the biases, or s_W
   // again without a bias; quads past N repeat the last one).
+  // Per-lane parts of those addresses that do not depend on the tile (row
+  // and column indices fit in 32 bits: N < 2^31, checked at launch).
+  const int n_last = (int)N - 1;
+  const int lrow = 16 * wave + (lane >> 4);              // tile row of block u: lrow + 4 u
+  const char* wbase = reinterpret_cast<const char*>(p.W);
+  const float* sbase = (lane >= 32 && p.bias) ? p.bias : p.sW;
+  const int squad = 4 * (lane & 31);
   auto issue = [&](int t) {
-    const int64_t n0 = (t_first + t) * kTileN;
+    const int n0 = (int)((t_first + t) * kTileN);
     const int st = t % S;
     const uint32_t sb = lds_base + (uint32_t)(st * kTileBytes);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int b = 4 * wave + u;
-      const int tr = 4 * b + (lane >> 4);
+      const int tr = lrow + 4 * u;
       const int chunk = (lane & 15) ^ (tr & 15);
-      const int64_t n = n0 + tr < N ? n0 + tr : N - 1;
-      dma16(reinterpret_cast<const int8_t*>(p.W) + n * kGroup + chunk * 16,
-            __builtin_amdgcn_readfirstlane(sb + b * 1024));
+      const int n = min(n0 + tr, n_last);
+      dma16(wbase + ((int64_t)n * kGroup + chunk * 16), __builtin_amdgcn_readfirstlane(sb + (4 * wave + u) * 1024));
     }
     if (five) {
-      const int64_t q = n0 + 4 * (lane & 31);
-      const int64_t qc = q < N ? q : N - 4;
-      const float* v = (lane >= 32 && p.bias) ? p.bias : p.sW;
-      dma16(v + qc, __builtin_amdgcn_readfirstlane(lds_base + L::kScales + (uint32_t)(st * 1024)));
+      const int q = min(n0 + squad, n_last - 3);
+      dma16(sbase + q, __builtin_amdgcn_readfirstlane(lds_base + L::kScales + (uint32_t)(st * 1024)));
     }
   };
 
@@ -316,8 +319,8 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float y = __fmul_rn((float)acc[j][r], __fmul_rn(sxv[j], sw[r]));
-        if (p.bias) y = __fadd_rn(y, bs[r]);
-        h[r] = __half_as_ushort(__float2half_rn(y));
+        if constexpr (kBias) y = __fadd_rn(y, bs[r]);
+        h[r] = __half_as_ushort(__float2half_rn(as_fp32(y)));
       }
       uint2 v;
       v.x = h[0] | (h[1] << 16);
@@ -347,9 +350,9 @@ BandPlan band_plan(int64_t M, int64_t N, int br) {
   return {br, groups, tpg};
 }
 
-template <int BR>
+template <int BR, bool kBias>
 hipError_t launch_br(const GemmArgs& a, const void* X, const BandPlan& bp, hipStream_t stream) {
-  auto fn = &band_kernel<BR>;
+  auto fn = &band_kernel<BR, kBias>;
   constexpr int lds = BandLayout<BR>::kBytes;
   if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(fn), lds); e != hipSuccess) return e;
   const int64_t bands = (a.M + BR - 1) / BR;
@@ -361,13 +364,13 @@ hipError_t launch_br(const GemmArgs& a, const void* X, const BandPlan& bp, hipSt
 }  // namespace
 
 bool band_fusable(int64_t M, int64_t N, int64_t K) {
-  return K == kGroup && M > 16 && M <= 2048 && N >= 4 && N % 4 == 0;
+  return K == kGroup && M > 16 && M <= 2048 && N >= 4 && N % 4 == 0 && N < ((int64_t)1 << 31);
 }
 
 hipError_t launch_band(const GemmArgs& a, const void* X, hipStream_t stream) {
   if (!band_fusable(a.M, a.N, a.K)) return hipErrorInvalidValue;
   const BandPlan bp = band_plan(a.M, a.N, kBandRows);
-  return launch_br<kBandRows>(a, X, bp, stream);
+  return a.bias ? launch_br<kBandRows, true>(a, X, bp, stream) : launch_br<kBandRows, false>(a, X, bp, stream);
 }
 
 }  // namespace convrot

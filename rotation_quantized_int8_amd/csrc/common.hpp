@@ -23,6 +23,17 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// x as a finished fp32 value in a register: the compiler can no longer fuse
+// the operation that produced x with the next one.  An fp32 product followed
+// by a conversion to fp16 would otherwise be folded into one mixed-precision
+// FMA (v_fma_mixlo_f16), which rounds the exact product once to fp16 instead
+// of first to fp32 -- a different result in rare cases (-ffp-contract=off
+// does not prevent it).
+__device__ __forceinline__ float as_fp32(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // fp64 -> fp16 with a single round-to-nearest-even.  The fp32 intermediate is
 // taken with round-to-odd (truncate, then force the last bit when inexact):
 // 24 >= 11 + 2 significand bits make the second rounding exact in effect.

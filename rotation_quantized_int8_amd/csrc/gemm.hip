@@ -150,7 +150,7 @@ splitk_epilogue_kernel(const int32_t* __restrict__ parts, int64_t splits, GemmAr
     float y = __fmul_rn((float)a[c], __fmul_rn(sx, p.sW[n]));
     if (p.bias) y = __fadd_rn(y, p.bias[n]);
     if (p.t_ld > 0) y = __fadd_rn(y, l[c]);
-    __half h = __float2half_rn(y);
+    __half h = __float2half_rn(as_fp32(y));
     if (p.R) h = __float2half_rn(__half2float(h) + __half2float(p.R[m * N + n]));
     hb[c] = __half_as_ushort(h);
   }

@@ -573,17 +573,17 @@ gemm_dma_kernel(GemmArgs p) {
         __half h[4];
         if constexpr (MODE == GemmMode::kI8toF16) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(yf[i][j][r]);
+          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(as_fp32(yf[i][j][r]));
         } else if constexpr (kW16) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float y = yf[i][j][r];
             if (p.bias) y = __fadd_rn(y, bsv[i][r]);
-            h[r] = EXTRA && p.out_bf16 ? __ushort_as_half(f32_to_bf16_rn(y)) : __float2half_rn(y);
+            h[r] = EXTRA && p.out_bf16 ? __ushort_as_half(f32_to_bf16_rn(y)) : __float2half_rn(as_fp32(y));
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(p.bias ? __fadd_rn(acc[i][j][r], bsv[i][r]) : acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(as_fp32(p.bias ? __fadd_rn(acc[i][j][r], bsv[i][r]) : acc[i][j][r]));
         }
         uint2 v;
         v.x = (uint32_t)__half_as_ushort(h[0]) | ((uint32_t)__half_as_ushort(h[1]) << 16);

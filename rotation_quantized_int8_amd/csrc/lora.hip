@@ -58,7 +58,7 @@ lora_down_kernel(const __half* __restrict__ X, const float* __restrict__ D, cons
       if (n >= N) continue;
       v4h h;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = (_Float16)(r + i < rank ? __fmul_rn(up[n * rank + r + i], scale) : 0.0f);
+      for (int i = 0; i < 4; ++i) h[i] = (_Float16)as_fp32(r + i < rank ? __fmul_rn(up[n * rank + r + i], scale) : 0.0f);
       *reinterpret_cast<v4h*>(U + n * t_ld + r) = h;
     }
     return;

@@ -246,7 +246,7 @@ skinny_kernel(GemmArgs p, const __half* __restrict__ Xf, int64_t kr, int rpb, in
       const int64_t n = nb + i < N ? nb + i : N - 1;
       float y = __fmul_rn((float)acc[c][i], __fmul_rn(sx, p.sW[n]));
       if (p.bias) y = __fadd_rn(y, p.bias[n]);
-      h[i] = __float2half_rn(y);
+      h[i] = __float2half_rn(as_fp32(y));
       if (p.R) h[i] = __float2half_rn(__half2float(h[i]) + __half2float(p.R[m * N + n]));
     }
     __half* Y = reinterpret_cast<__half*>(p.out) + m * N + nb;
