@@ -145,7 +145,8 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
   constexpr int S = L::S;
   constexpr int FM = BR / 16;                      // 16-row MFMA blocks of the band
   extern __shared__ __align__(16) char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
   const int frow = lane & 15, fk = lane >> 4;
   const int64_t M = p.M, N = p.N;
   const int64_t g = (int64_t)blockIdx.x % groups;
@@ -162,26 +163,39 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
   // 0-31: s_W of the tile's columns in quads, 32-63: the biases, or s_W
   // again without a bias; quads past N repeat the last one).
   // Per-lane parts of those addresses that do not depend on the tile (row
-  // and column indices fit in 32 bits: N < 2^31, checked at launch).
+  // and column indices fit in 32 bits: N < 2^31, checked at launch): block
+  // u's source in tile 0 of the group; tile t adds t whole tiles, unless the
+  // tile reaches past N (then the rows are clamped one by one).
   const int n_last = (int)N - 1;
   const int lrow = 16 * wave + (lane >> 4);              // tile row of block u: lrow + 4 u
   const char* wbase = reinterpret_cast<const char*>(p.W);
   const float* sbase = (lane >= 32 && p.bias) ? p.bias : p.sW;
   const int squad = 4 * (lane & 31);
+  const char* wsrc0[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int tr = lrow + 4 * u;
+    wsrc0[u] = wbase + ((int64_t)(t_first * kTileN + tr) * kGroup + (((lane & 15) ^ (tr & 15)) << 4));
+  }
   auto issue = [&](int t) {
     const int n0 = (int)((t_first + t) * kTileN);
     const int st = t % S;
     const uint32_t sb = lds_base + (uint32_t)(st * kTileBytes);
+    if (n0 + kTileN <= N) {   // whole tile
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int tr = lrow + 4 * u;
-      const int chunk = (lane & 15) ^ (tr & 15);
-      const int n = min(n0 + tr, n_last);
-      dma16(wbase + ((int64_t)n * kGroup + chunk * 16), __builtin_amdgcn_readfirstlane(sb + (4 * wave + u) * 1024));
+      for (int u = 0; u < 4; ++u)
+        dma16(wsrc0[u] + (int64_t)t * kTileBytes, sb + (uint32_t)((4 * wave + u) * 1024));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tr = lrow + 4 * u;
+        const int n = min(n0 + tr, n_last);
+        dma16(wbase + ((int64_t)n * kGroup + (((lane & 15) ^ (tr & 15)) << 4)), sb + (uint32_t)((4 * wave + u) * 1024));
+      }
     }
     if (five) {
       const int q = min(n0 + squad, n_last - 3);
-      dma16(sbase + q, __builtin_amdgcn_readfirstlane(lds_base + L::kScales + (uint32_t)(st * 1024)));
+      dma16(sbase + q, lds_base + L::kScales + (uint32_t)(st * 1024));
     }
   };
 
@@ -269,11 +283,22 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
           if (p.R) v = add_f16x8(v, *reinterpret_cast<const v4i*>(p.R + m * N + n));
           __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));
         } else {
-          const __half* hv = reinterpret_cast<const __half*>(&v);
-          for (int e = 0; e < 8 && n + e < N; ++e) {
-            __half o = hv[e];
-            if (p.R) o = __float2half_rn(__half2float(o) + __half2float(p.R[m * N + n + e]));
-            dst[e] = o;
+          // N is a multiple of 4: rows start 8-byte aligned, and each 4-column
+          // half of the piece is in range or wholly past N
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (n + 4 * q >= N) break;
+            uint2 o = q == 0 ? make_uint2(v.x, v.y) : make_uint2(v.z, v.w);
+            if (p.R) {
+              const uint2 r = *reinterpret_cast<const uint2*>(p.R + m * N + n + 4 * q);
+              const __half* a = reinterpret_cast<const __half*>(&o);
+              const __half* b = reinterpret_cast<const __half*>(&r);
+              __half z[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) z[e] = __float2half_rn(__half2float(a[e]) + __half2float(b[e]));
+              o = *reinterpret_cast<const uint2*>(z);
+            }
+            *reinterpret_cast<uint2*>(dst + 4 * q) = o;
           }
         }
       }
