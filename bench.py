@@ -616,6 +616,11 @@ def main():
         w16 = w.to(torch.float16)
         del w
         qws = [qw] + [qw.clone() for _ in range(layers - 1)]   # one weight buffer per layer
+        # the fp16 baselines get their own weights per layer too (3.6 GiB in
+        # all, far beyond the 256 MiB memory-side cache): with one matrix
+        # shared by all layers of a shape they would read cached weights
+        # while the W8A8 step streams its own from HBM every layer
+        w16s = ([w16] + [w16.clone() for _ in range(layers - 1)]) if not (args.no_compare or args.profile_kernels) else [w16]
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
         ws8 = torch.empty(cr.workspace_bytes(cr.PATH_W8A8, M, N, K), dtype=torch.uint8, device=dev)
         ws16 = torch.empty(cr.workspace_bytes(cr.PATH_W8A16, M, N, K, wl.LORA_RANK), dtype=torch.uint8, device=dev)
@@ -626,7 +631,7 @@ def main():
         # Q_X / s_X of the stand-alone prologue and GEMM legs
         qx = torch.empty((M, K), dtype=torch.int8, device=dev)
         sx = torch.empty(M, dtype=torch.float32, device=dev)
-        per_shape.append(dict(N=N, K=K, layers=layers, x=x, qws=qws, sw=sw, w16=w16, y=y, ws8=ws8,
+        per_shape.append(dict(N=N, K=K, layers=layers, x=x, qws=qws, sw=sw, w16=w16, w16s=w16s, y=y, ws8=ws8,
                               ws8l=ws8l, wsd=wsd, wsr=wsr, ws16=ws16, xb=x.to(torch.bfloat16),
                               yb=torch.empty((M, N), dtype=torch.bfloat16, device=dev), down=down.to(dev), up=up.to(dev), qx=qx, sx=sx,
                               bias=wl.make_bias(N, seed=0).to(dev), res=wl.make_residual(M, N, seed=0).to(dev)))
@@ -827,13 +832,19 @@ def main():
             def own_f16_step():
                 h = torch.cuda.current_stream().cuda_stream
                 for s in per_shape:
-                    for _ in s["qws"]:
-                        L.convrot_gemm_f16(s["x"].data_ptr(), s["w16"].data_ptr(), M, s["N"], s["K"],
+                    for w in s["w16s"]:
+                        L.convrot_gemm_f16(s["x"].data_ptr(), w.data_ptr(), M, s["N"], s["K"],
                                            s["y"].data_ptr(), h)
 
             def torch_f16_step():
                 for s in per_shape:
-                    for _ in s["qws"]:
+                    for w in s["w16s"]:
+                        F.linear(s["x"], w)
+
+            def torch_f16_shared_step():
+                # one fp16 matrix for all layers of a shape: cached weights
+                for s in per_shape:
+                    for _ in s["w16s"]:
                         F.linear(s["x"], s["w16"])
 
             for name, fn in (("w8a8_bias_residual", w8a8_bias_res_step),
@@ -841,7 +852,8 @@ def main():
                              ("w8a16_lora32", w8a16_step), ("w8a16_rangesafe_bf16", w8a16_rs_step),
                              ("dequant_every_call", dequant_step),
                              ("fp16_own_mfma", own_f16_step),
-                             ("fp16_torch_linear", torch_f16_step)):
+                             ("fp16_torch_linear", torch_f16_step),
+                             ("fp16_torch_linear_shared_weights", torch_f16_shared_step)):
                 gc = capture(fn, stream)
                 t = timed_graph(gc, args.steps, args.warmup, stream)
                 del gc
@@ -928,6 +940,9 @@ def main():
         "per_shape": shape_rows,
         "weighted_total_ms": round(sum(r["w8a8_us"] * r["layers"] for r in shape_rows) / 1e3, 4),
         "compare": compare,
+        "compare_note": "448-layer sweeps timed like the W8A8 step; every leg reads its own weights per "
+                        "layer (int8 or fp16), except fp16_torch_linear_shared_weights, which reuses one "
+                        "fp16 matrix for all layers of a shape",
         "m_sweep": msweep,
     }
     if not args.no_cpu_baseline:
