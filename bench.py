@@ -760,7 +760,7 @@ def main():
         # Per shape, the pages' protocol: 20 back-to-back calls on hot buffers,
         # timed as 7 sets; median per call.  Graph-captured, so launch cost is
         # the in-graph dispatch cost, as in the step above.
-        log("per-shape timings (median of 7 sets of 20 calls)")
+        log("per-shape timings (median of 7 sets of 20 calls; then each shape's layers with their own weights)")
         shape_rows = []
         for s in per_shape:
             N, K = s["N"], s["K"]
@@ -796,6 +796,28 @@ def main():
             row["gemm_tops"] = round(2.0 * M * N * K / (row["gemm_i8_f16_us"] * 1e-6) / 1e12, 1)
             row["gemm_frac_of_int8_peak"] = round(row["gemm_tops"] / PEAK_INT8_TOPS, 4)
             row["w8a8_frac_of_int8_peak"] = round(row["w8a8_tops"] / PEAK_INT8_TOPS, 4)
+            if not args.no_compare:
+                # the shape's layers back to back, each call with its own
+                # weights (as in the step): W8A8 and the two fp16 GEMMs
+                def own(fn_w, ws_):
+                    def run():
+                        h = torch.cuda.current_stream().cuda_stream
+                        for w in ws_:
+                            fn_w(h, w)
+                    return run
+                cold = {
+                    "w8a8_own_weights": own(lambda h, w: f8a8(x.data_ptr(), M, K, w.data_ptr(), s["sw"].data_ptr(),
+                                                              N, None, y.data_ptr(), s["ws8"].data_ptr(),
+                                                              s["ws8"].numel(), h), s["qws"]),
+                    "fp16_own_mfma_own_weights": own(lambda h, w: L.convrot_gemm_f16(x.data_ptr(), w.data_ptr(), M, N, K,
+                                                                                     y.data_ptr(), h), s["w16s"]),
+                    "fp16_torch_linear_own_weights": own(lambda h, w: F.linear(x, w), s["w16s"]),
+                }
+                for name, fn in cold.items():
+                    gs = capture(fn, stream)
+                    t = median_sets(gs, 7, stream) / len(s["qws"])
+                    del gs
+                    row[name + "_us"] = round(t * 1e3, 3)
             shape_rows.append(row)
 
         compare = {}
@@ -938,6 +960,9 @@ def main():
         },
         "device_peak": device_peak_int8_tops(dev.index or 0),
         "per_shape": shape_rows,
+        "per_shape_note": "*_us without a suffix: the pages' protocol (20 back-to-back calls on the same buffers, "
+                          "median of 7 sets); *_own_weights_us: the shape's layers back to back, each call with "
+                          "its own weights (int8, or fp16 copies) as in the step, median of 7 sets",
         "weighted_total_ms": round(sum(r["w8a8_us"] * r["layers"] for r in shape_rows) / 1e3, 4),
         "compare": compare,
         "compare_note": "448-layer sweeps timed like the W8A8 step; every leg reads its own weights per "

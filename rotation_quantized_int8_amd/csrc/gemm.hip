@@ -9,12 +9,17 @@ namespace convrot {
 
 // 256x128 tiles read half the operand bytes per output of 128x64 tiles,
 // which pays once they still give most of the 256 CUs a tile; otherwise
-// 128x64 tiles spread the work wider (as 8 waves of 32x32 with 256-byte K
-// slices: two waves per SIMD and half the slice barriers, 5 % faster than 4
-// waves of 64x32 for the int8 product on 2048x2048 and 6-10 % for the fp16
-// one; the weight-only product, which widens its int8 weights per wave,
-// keeps 4 waves), and when even those would leave half the CUs idle, 64x64
-// or 32x64 tiles do.  The 256x128 tile runs as 8 waves
+// 128x64 tiles spread the work wider (as 8 waves of 32x32: two waves per
+// SIMD, 5 % faster than 4 waves of 64x32 for the int8 product on 2048x2048
+// and 6-10 % for the fp16 one; the weight-only product, which widens its int8
+// weights per wave, keeps 4 waves), and when even those would leave half the
+// CUs idle, 64x64 or 32x64 tiles do.  The 8-wave 128x64 tile streams the
+// int8 product in 128-byte K slices on a 4-stage ring (96 KiB): against 3
+// stages of 256-byte slices (144 KiB) the first slice lands sooner, which
+// measured 0.5-2.8 % faster per layer at 2048x2048 and 2048x1024 (M = 1024,
+// each layer its own weights or the same ones) and level at 2048x8192; the
+// fp16 product keeps the 256-byte slices (half the barriers for its longer
+// rows).  The 256x128 tile runs as 8 waves
 // of 64x64 (two per SIMD, so one wave's waits overlap the other's MFMAs).
 // With at most two 128-byte K slices (K <= 256) an int8 tile is one
 // serial fill, product, epilogue and store; 128x128 tiles on a two-stage
@@ -41,7 +46,7 @@ int choose_gemm_cfg(GemmMode mode, int64_t M, int64_t N, int64_t K) {
   const bool int8 = mode == GemmMode::kI8toF16 || mode == GemmMode::kI8toI32;
   if (mode == GemmMode::kI8toF16 && K <= 256 && tiles(128, 128) >= 256) return 21;
   if (tiles(256, 128) >= 160) return 13;
-  if (tiles(128, 64) >= 128) return mode == GemmMode::kW8A16 ? 8 : 20;
+  if (tiles(128, 64) >= 128) return mode == GemmMode::kW8A16 ? 8 : (int8 ? 22 : 20);
   if (tiles(64, 64) >= 128) return 10;
   if (int8 && tiles(32, 64) < 256) return 19;
   return 9;

@@ -701,7 +701,9 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
         case 13: return launch_cfg<MODE, 4, 2, 4, 4, 3, true>(a, stream);
         case 21: return launch_cfg<MODE, 4, 2, 4, 4, 3, true>(a, stream);   // extras: the 256x128 tile
         case 19: return launch_cfg<MODE, 2, 2, 1, 1, 4, true, 256>(a, stream);
-        case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, true, 256>(a, stream);
+        case 22:
+          if constexpr (MODE == GemmMode::kI8toF16) return launch_cfg<MODE, 4, 2, 2, 2, 4, true, 128>(a, stream);
+          return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
       }
     }
@@ -718,7 +720,13 @@ hipError_t launch_gemm_dma_cfg(const GemmArgs& a, int cfg, hipStream_t stream) {
         return launch_cfg<MODE, 2, 2, 4, 4, 2>(a, stream);
       return hipErrorInvalidValue;
     case 19: return launch_cfg<MODE, 2, 2, 1, 1, 4, false, 256>(a, stream);  // 32x32, 256-byte K slices
-    case 20: return launch_cfg<MODE, 4, 2, 2, 2, 3, false, 256>(a, stream);  // 128x64, 8 waves of 32x32, 256-byte K slices
+    case 20:   // 128x64, 8 waves of 32x32, 256-byte K slices on 3 stages: fp16 product
+      if constexpr (MODE == GemmMode::kF16) return launch_cfg<MODE, 4, 2, 2, 2, 3, false, 256>(a, stream);
+      return hipErrorInvalidValue;
+    case 22:   // 128x64, 8 waves of 32x32, 128-byte K slices on 4 stages: int8 products
+      if constexpr (MODE == GemmMode::kI8toF16 || MODE == GemmMode::kI8toI32)
+        return launch_cfg<MODE, 4, 2, 2, 2, 4, false, 128>(a, stream);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
