@@ -120,26 +120,29 @@ __device__ __forceinline__ void rotate_group(const __half* __restrict__ src, cha
 
 // Exact-definition quantisation of 16 fp32 values with scale s (> 0, or 0
 // for an all-zero row, whose codes are 0):
-// q = round_half_even(fp32(v / s)).  The fast path multiplies by the
-// reciprocal; when any product lies within 3e-5 of a half-integer -- closer
-// than its possible deviation from the correctly rounded quotient -- the
-// lane falls back to IEEE division for its 16 values.  The rounding to an
-// integer is one fp32 addition of 1.5 * 2^23: for |t| < 2^22 the sum rounds
-// t half to even at the units place and holds the integer, two's complement,
-// in its low mantissa bits, so the low byte of the sum's bits is the int8
-// code.  |v / s| <= 127 (1 + 2^-23) for finite inputs, so no clamp is needed.
-// With s = 0 the reciprocal is taken as 0, so every t is 0 and the codes are
-// 0 without a separate path.
+// q = round_half_even(fp32(v / s)).  The fast path rounds the exact product
+// v r, with r the hardware reciprocal of s (within one ulp of 1 / s), to an
+// integer in one step: m = fma(v, r, 1.5 * 2^23) rounds v r + 1.5 * 2^23 once,
+// and for |v r| < 2^22 the units place of that sum is where v r gets rounded,
+// half to even; the integer k = m - 1.5 * 2^23 sits, two's complement, in the
+// low mantissa bits of m, so the low byte of m's bits is the int8 code.  For
+// finite inputs |v / s| <= 127 (1 + 2^-23), so v r is within 1.6e-5 of v / s
+// and fp32(v / s) within 3.9e-6: whenever v r lies more than 3e-5 from a
+// half-integer, both round to the same integer.  d = fma(v, r, -k), the
+// distance v r - k rounded once, detects the rest: when any |d| > 0.49997 the
+// lane falls back to IEEE division for its 16 values.  No clamp is needed.
+// With s = 0 the reciprocal is taken as 0, so every product is 0 and the
+// codes are 0 without a separate path.
 __device__ __forceinline__ uint4 quantize16(const float (&v)[16], float s) {
   constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
-  const float rcp = s == 0.0f ? 0.0f : 1.0f / s;
+  const float rcp = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
   uint32_t b[16];
   float dmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float t = __fmul_rn(v[i], rcp);
-    const float m = __fadd_rn(t, kMagic);
-    dmax = fmaxf(dmax, fabsf(__fsub_rn(t, __fsub_rn(m, kMagic))));
+    const float m = __fmaf_rn(v[i], rcp, kMagic);
+    const float k = __fsub_rn(m, kMagic);   // exact: an integer of at most 8 bits
+    dmax = fmaxf(dmax, fabsf(__fmaf_rn(v[i], rcp, -k)));
     b[i] = __float_as_uint(m);
   }
   if (dmax > 0.49997f) {
