@@ -340,16 +340,15 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
     char* sbw = smem + L::kStage + (t & 1) * BR * kStageRow;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      uint32_t h[4];
+      float y[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float y = __fmul_rn((float)acc[j][r], __fmul_rn(sxv[j], sw[r]));
-        if constexpr (kBias) y = __fadd_rn(y, bs[r]);
-        h[r] = __half_as_ushort(__float2half_rn(as_fp32(y)));
+        y[r] = __fmul_rn((float)acc[j][r], __fmul_rn(sxv[j], sw[r]));
+        if constexpr (kBias) y[r] = __fadd_rn(y[r], bs[r]);
       }
       uint2 v;
-      v.x = h[0] | (h[1] << 16);
-      v.y = h[2] | (h[3] << 16);
+      v.x = pack_f16x2_rn(y[0], y[1]);
+      v.y = pack_f16x2_rn(y[2], y[3]);
       const int row = 16 * j + frow;
       *reinterpret_cast<uint2*>(sbw + row * kStageRow + (((2 * wave + (fk >> 1)) ^ (row & 15)) << 4) + 8 * (fk & 1)) = v;
     }

@@ -34,6 +34,17 @@ __device__ __forceinline__ float as_fp32(float x) {
   return x;
 }
 
+// Two finished fp32 values to fp16, each rounded once to nearest even as
+// __float2half_rn does, packed low then high: one v_cvt_pk_f16_f32 (checked
+// bit for bit against the scalar conversion over every fp32 bit pattern,
+// NaNs compared as NaNs).
+__device__ __forceinline__ uint32_t pack_f16x2_rn(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 h = __builtin_convertvector((f2){as_fp32(a), as_fp32(b)}, h2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // fp64 -> fp16 with a single round-to-nearest-even.  The fp32 intermediate is
 // taken with round-to-odd (truncate, then force the last bit when inexact):
 // 24 >= 11 + 2 significand bits make the second rounding exact in effect.

@@ -570,24 +570,27 @@ gemm_dma_kernel(GemmArgs p) {
       if constexpr (MODE == GemmMode::kI8toI32) {
         *reinterpret_cast<v4i*>(d) = acc[i][j];
       } else {
-        __half h[4];
+        uint2 v;
         if constexpr (MODE == GemmMode::kI8toF16) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(as_fp32(yf[i][j][r]));
+          v.x = pack_f16x2_rn(yf[i][j][0], yf[i][j][1]);
+          v.y = pack_f16x2_rn(yf[i][j][2], yf[i][j][3]);
         } else if constexpr (kW16) {
+          __half h[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float y = yf[i][j][r];
             if (p.bias) y = __fadd_rn(y, bsv[i][r]);
             h[r] = EXTRA && p.out_bf16 ? __ushort_as_half(f32_to_bf16_rn(y)) : __float2half_rn(as_fp32(y));
           }
+          v.x = (uint32_t)__half_as_ushort(h[0]) | ((uint32_t)__half_as_ushort(h[1]) << 16);
+          v.y = (uint32_t)__half_as_ushort(h[2]) | ((uint32_t)__half_as_ushort(h[3]) << 16);
         } else {
+          float y[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = __float2half_rn(as_fp32(p.bias ? __fadd_rn(acc[i][j][r], bsv[i][r]) : acc[i][j][r]));
+          for (int r = 0; r < 4; ++r) y[r] = p.bias ? __fadd_rn(acc[i][j][r], bsv[i][r]) : acc[i][j][r];
+          v.x = pack_f16x2_rn(y[0], y[1]);
+          v.y = pack_f16x2_rn(y[2], y[3]);
         }
-        uint2 v;
-        v.x = (uint32_t)__half_as_ushort(h[0]) | ((uint32_t)__half_as_ushort(h[1]) << 16);
-        v.y = (uint32_t)__half_as_ushort(h[2]) | ((uint32_t)__half_as_ushort(h[3]) << 16);
         *reinterpret_cast<uint2*>(d) = v;
       }
     }
