@@ -131,10 +131,11 @@ size_t convrot_workspace_bytes(int path, int64_t M, int64_t N, int64_t K, int64_
  * optional bias fp32 [N] (NULL = none) -> Y fp16 [M, N].  Runs the fused
  * rotate/absmax/quantise prologue (Q_X and s_X go to the workspace) and the
  * int8 MFMA GEMM with the scale epilogue -- or, when every row is a single
- * rotation group (K = 256, 16 < M <= 2048, N a multiple of 4) or there are
- * few short rows (M <= 16, M K <= 8192), one launch that quantises the rows
- * in each workgroup and leaves the workspace unused.  The result is the same
- * bits on every path. */
+ * rotation group (K = 256, 16 < M <= 2048, N a multiple of 4), the layer is
+ * narrow (K = 512 or 1024, M > 16, 4 <= N <= 256 with N a multiple of 4,
+ * ceil(M / 8) ceil(N / 128) <= 256) or there are few short rows (M <= 16,
+ * M K <= 8192), one launch that quantises the rows in each workgroup and
+ * leaves the workspace unused.  The result is the same bits on every path. */
 convrot_status convrot_linear_w8a8(const void* X, int64_t M, int64_t K,
                                    const int8_t* Q_W, const float* s_W, int64_t N,
                                    const float* bias, void* Y,

@@ -348,6 +348,13 @@ convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_
     g.M = M; g.N = N; g.K = K;
     return launched(launch_band(g, X, s));
   }
+  if (plan.kind == W8A8Plan::kNarrow) {  // one launch over row bands (narrow layers)
+    GemmArgs g{};
+    g.W = Q_W; g.sW = s_W; g.bias = bias; g.out = Y;
+    g.R = reinterpret_cast<const __half*>(residual);
+    g.M = M; g.N = N; g.K = K;
+    return launched(launch_narrow(g, X, s));
+  }
   if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s))) return st;
   if (lora) {
     if (convrot_status st = launched(launch_lora_prep(X, lora->down, lora->up, lora->scale, M, N, K,

@@ -79,6 +79,7 @@ int64_t w8a8_splits(int64_t M, int64_t N, int64_t K) {
 W8A8Plan w8a8_plan(int64_t M, int64_t N, int64_t K, bool lora) {
   if (!lora && skinny_fusable(M, K)) return {W8A8Plan::kFused, 1, false};
   if (!lora && band_fusable(M, N, K)) return {W8A8Plan::kBand, 1, false};
+  if (!lora && narrow_fusable(M, N, K)) return {W8A8Plan::kNarrow, 1, false};
   if (M <= 8 && N <= 4096) {
     const int64_t s = skinny_splits(M, N, K);
     return {W8A8Plan::kSkinny, s, lora || s > 1};

@@ -50,18 +50,25 @@ hipError_t launch_skinny_fused(const GemmArgs& a, const void* X, hipStream_t str
 // activation [M, 256].
 bool band_fusable(int64_t M, int64_t N, int64_t K);
 hipError_t launch_band(const GemmArgs& a, const void* X, hipStream_t stream);
+// The whole W8A8 layer in one launch for narrow layers: K = 512 or 1024,
+// M > 16, 4 <= N <= 256 with N % 4 == 0, and ceil(M / 8) ceil(N / 128) <= 256
+// workgroups; each quantises its band of 8 rows itself (a.X and a.sX are
+// unused, X is the fp16 activation [M, K]).
+bool narrow_fusable(int64_t M, int64_t N, int64_t K);
+hipError_t launch_narrow(const GemmArgs& a, const void* X, hipStream_t stream);
 
 // Split-K plan of the W8A8 tiled-GEMM path with few rows (M <= 128; 1 = no
 // split, always for more rows).
 int64_t w8a8_splits(int64_t M, int64_t N, int64_t K);
 
 // How the W8A8 linear runs for a size: one fused launch (few rows, short
-// rows, no LoRA), one fused launch over row bands (K = 256, no LoRA), the
+// rows, no LoRA), one fused launch over row bands (K = 256, or narrow layers
+// with K = 512 / 1024; no LoRA), the
 // prologue and the few-row kernel (M <= 8, N <= 4096), or the prologue and
 // the tiled GEMM; `parts` says whether int32 partials [splits, M, N] go
 // through the workspace to the K-split epilogue.
 struct W8A8Plan {
-  enum Kind { kFused, kBand, kSkinny, kGemm } kind;
+  enum Kind { kFused, kBand, kNarrow, kSkinny, kGemm } kind;
   int64_t splits;
   bool parts;
 };

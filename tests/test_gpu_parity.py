@@ -757,6 +757,66 @@ def test_linear_w8a8_band_residual_in_place(M, N):
     assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
 
 
+# ------------------------- one-launch layer for narrow layers (next-1)
+# With K = 512 or 1024 and N <= 256, while ceil(M / 8) ceil(N / 128) <= 256,
+# the layer runs as one launch in which every workgroup quantises its band
+# of 8 rows itself (twice per band when N > 128).  Cases cover a single
+# ragged band, ragged 128-column groups, rows that are not 16-byte aligned
+# (N % 8 = 4), both K, bias, heavy-tailed rows, and the largest grid
+# (2048 x 128) next to a size just past it (2048 x 256, two launches).
+
+@pytest.mark.parametrize("M,N,K,bias,dist", [(17, 4, 512, False, "normal"), (33, 100, 1024, True, "t3"),
+                                             (64, 128, 512, False, "normal"), (100, 252, 1024, False, "t3"),
+                                             (513, 256, 512, True, "normal"), (777, 132, 512, True, "normal"),
+                                             (1000, 200, 1024, False, "normal"), (1024, 256, 1024, True, "t3"),
+                                             (2048, 128, 1024, False, "normal"), (2048, 256, 1024, True, "normal")])
+def test_linear_w8a8_narrow_bitexact(M, N, K, bias, dist):
+    _say(f"linear w8a8 one launch narrow M={M} N={N} K={K} bias={bias} {dist}")
+    mism, emax, rel = _w8a8_case(M, N, K, seed=M * 5 + N + K, dist=dist, bias=bias)
+    assert mism == 0 and emax == 0.0
+
+
+@pytest.mark.parametrize("K", [512, 1024])
+def test_linear_w8a8_narrow_special_rows(K):
+    # rounding-tie rows (their first group decides the row scale; the rest of
+    # the row is zero), a zero row, fp16 extremes, subnormals and a constant
+    # row, in the first band and into a ragged second one
+    _say(f"linear w8a8 one launch narrow K={K} special rows")
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+    rows = []
+    for r in g["tie_rows"]["rows"]:
+        x = np.zeros(K)
+        x[0:256:2] = r["x_even_num"] / r["den"]
+        x[1:256:2] = r["x_odd_num"] / r["den"]
+        rows.append(x)
+    rows.append(np.zeros(K))
+    rows.append(np.full(K, 65504.0))
+    rows.append(np.full(K, -65504.0))
+    rows.append(np.where(np.arange(K) % 3 == 0, 2.0 ** -24, -(2.0 ** -24)))
+    rows.append(np.full(K, 0.5))
+    rest = wl.make_activations(21 - len(rows), K, seed=79).numpy().astype(np.float64)
+    x = np.concatenate([np.array(rows), rest]).astype(np.float16)
+    w = wl.make_weights(136, K, seed=80)
+    qw, sw = O.quantize_weights(w.numpy())
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    yg = _np(cr.linear_w8a8(t(x), t(qw), t(sw)))
+    with np.errstate(over="ignore"):   # the fp16-max rows overflow Y to +-inf on both sides
+        yo, qx, sx, a = O.linear_w8a8(x, qw, sw, None)
+    assert list(qx[:4, 1]) == [r["Q_X_1"] for r in g["tie_rows"]["rows"]]
+    assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+    assert not yg[4].any()
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 100, 1024), (300, 252, 512), (1024, 256, 1024)])
+def test_linear_w8a8_narrow_residual_in_place(M, N, K):
+    # bias and an fp16 residual that is the output buffer itself
+    _say(f"linear w8a8_ex one launch narrow in place M={M} N={N} K={K}")
+    yg, yo, tol = _w8a8_ex_case(M, N, K, seed=M + N + K, bias=True, in_place=True)
+    assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
+
+
 # ------------------------------------------ few activation rows (next-1)
 # M <= 16 with M K <= 8192 runs as one fused launch; M <= 16 with N <= 4096
 # otherwise runs the prologue and the few-row kernel (K split into int32
