@@ -56,13 +56,15 @@ def _noalloc(L, x, qw, sw, b, y, h):
 # (first, second): the second call is smaller.  Paths: the tiled GEMM
 # (1024 rows), the few-row GEMM with int32 K-split partials in the scratch
 # (16 x 2048 x 8192: 4 K ranges), the few-row kernel, the one-launch path for
-# few short rows, and the one-launch path for K = 256 (each workgroup
-# quantises its own band of rows; no scratch), then a ragged one.
+# few short rows, and the one-launch paths for K = 256 and for narrow
+# layers (each workgroup quantises its own band of rows; no scratch), each
+# followed by a ragged one.
 PAIRS = [((1024, 2048, 2048), (300, 203, 768)),
          ((1024, 8192, 2048), (16, 2048, 8192)),
          ((16, 2048, 8192), (4, 256, 8192)),
          ((4094, 2048, 8192), (1, 8192, 2048)),
-         ((1024, 6144, 256), (100, 252, 256))]
+         ((1024, 6144, 256), (100, 252, 256)),
+         ((1024, 256, 1024), (100, 132, 512))]
 
 
 @pytest.mark.parametrize("first,second", PAIRS)
