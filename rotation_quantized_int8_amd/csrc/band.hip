@@ -7,13 +7,14 @@
 // With K = 256 a row's quantisation needs only that row, so a workgroup can
 // quantise the rows it multiplies itself: the layer needs no second launch
 // and no Q_X round trip through memory.  A workgroup (8 wavefronts) owns a
-// band of 32 activation rows and a group of 128-column weight tiles; the
-// column groups of a band each quantise the band again, so the grid is sized
-// to about one workgroup per CU (bands x groups ~ 256) and a group is as
-// wide as that allows (the repeated rotation is a fixed ~2.6 k vector cycles
-// per workgroup, while narrower groups would re-read more weight bytes).
+// band of 32 activation rows (16 when M <= 128) and a group of 128-column
+// weight tiles; the column groups of a band each quantise the band again, so
+// the grid is sized to about one workgroup per CU (bands x groups ~ 256) and
+// a group is as wide as that allows (the repeated rotation is a fixed ~2.6 k
+// vector cycles per workgroup, while narrower groups would re-read more
+// weight bytes).
 //
-// Per workgroup (BR = 32 rows):
+// Per workgroup (BR = 32 rows; with 16, segments 16-31 skip steps 1-2):
 //   1. every lane loads its part of the band (16-lane segments, one row
 //      each) and parks it in its segment's LDS slot; then the direct
 //      global->LDS loads of weight tiles 0 and 1 go out (each tile 128 rows
@@ -176,11 +177,12 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
   const int seg = tid >> 4, l16 = tid & 15;
   char* slot = smem + L::kSlots + seg * kSlotBytes;
   float* sxs = reinterpret_cast<float*>(smem + L::kSx);
-  constexpr int Q = BR / kSegs;
+  constexpr int Q = (BR + kSegs - 1) / kSegs;        // segments past BR (BR = 16) idle
   v4i xr[Q][2];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
-    const int64_t m = m0 + kSegs * q + seg < M ? m0 + kSegs * q + seg : M - 1;
+    const int jl = BR >= kSegs || kSegs * q + seg < BR ? kSegs * q + seg : BR - 1;
+    const int64_t m = m0 + jl < M ? m0 + jl : M - 1;
     const v4i* src = reinterpret_cast<const v4i*>(X + m * kGroup + 16 * l16);
     xr[q][0] = __builtin_nontemporal_load(src);
     xr[q][1] = __builtin_nontemporal_load(src + 1);
@@ -191,13 +193,15 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int j = kSegs * q + seg;
-    park_row(slot, l16, xr[q][0], xr[q][1]);
+    const bool idle = BR < kSegs && j >= BR;   // whole wavefronts (BR = 16: wavefronts 4-7)
+    if (!idle) park_row(slot, l16, xr[q][0], xr[q][1]);
     if (q == 0) {
       compiler_fence();
 #pragma unroll
       for (int t = 0; t < L::F; ++t)
         if (t < T) issue(t);
     }
+    if (idle) continue;
     double y[16];
     rotate_staged(slot, l16, y);
     float f[16];
@@ -236,15 +240,15 @@ band_kernel(GemmArgs p, const __half* X, int64_t groups, int64_t tpg) {
   const bool vec_rows = (N % 8) == 0;   // every output row starts 16-byte aligned
   __half* Y = reinterpret_cast<__half*>(p.out);
   // Tile u's output from staging tile u & 1: BR rows x 16 pieces of 16 bytes,
-  // BR / 32 per thread (rows tid / 16 + 32 h, columns n0 + 8 (tid % 16) ..),
-  // [+ the residual] to Y.
+  // one per thread and 32 rows at a time (rows tid / 16 + 32 h, columns
+  // n0 + 8 (tid % 16) ..), [+ the residual] to Y.
   auto store_tile = [&](int u) {
     const char* sb = smem + L::kStage + (u & 1) * BR * kStageRow;
 #pragma unroll
-    for (int h = 0; h < BR / 32; ++h) {
+    for (int h = 0; h < (BR + 31) / 32; ++h) {
       const int rl = (tid >> 4) + 32 * h, pc = tid & 15;
       const int64_t m = m0 + rl, n = (t_first + u) * kTileN + 8 * pc;
-      if (m < M && n < N) {
+      if ((BR % 32 == 0 || rl < BR) && m < M && n < N) {
         v4i v = *reinterpret_cast<const v4i*>(sb + rl * kStageRow + ((pc ^ (rl & 15)) << 4));
         __half* dst = Y + m * N + n;
         if (vec_rows && n + 8 <= N) {
@@ -359,8 +363,15 @@ bool band_fusable(int64_t M, int64_t N, int64_t K) {
   return K == kGroup && M > 16 && M <= 2048 && N >= 4 && N % 4 == 0 && N < ((int64_t)1 << 31);
 }
 
+// Bands of 32 rows; with at most 128 rows, bands of 16 (half the segments
+// rotate, twice the bands share the CUs): 5-15 % faster there (17, 100 and
+// 128 rows), 5-29 % slower from 512 rows on.
 hipError_t launch_band(const GemmArgs& a, const void* X, hipStream_t stream) {
   if (!band_fusable(a.M, a.N, a.K)) return hipErrorInvalidValue;
+  if (a.M <= 128) {
+    const BandPlan bp = band_plan(a.M, a.N, 16);
+    return a.bias ? launch_br<16, true>(a, X, bp, stream) : launch_br<16, false>(a, X, bp, stream);
+  }
   const BandPlan bp = band_plan(a.M, a.N, kBandRows);
   return a.bias ? launch_br<kBandRows, true>(a, X, bp, stream) : launch_br<kBandRows, false>(a, X, bp, stream);
 }
