@@ -717,11 +717,13 @@ def test_linear_w8a8_band_bitexact(M, N, bias, dist):
     assert mism == 0 and emax == 0.0
 
 
-def test_linear_w8a8_band_special_rows():
+@pytest.mark.parametrize("M", [40, 200])
+def test_linear_w8a8_band_special_rows(M):
     # rounding-tie rows (their first group, whose maximum decides the row
-    # scale), a zero row, fp16 extremes, subnormals and a constant row,
-    # filling a ragged second band
-    _say("linear w8a8 one launch K=256 special rows")
+    # scale), a zero row, fp16 extremes, subnormals and a constant row, then
+    # ordinary rows into a ragged last band (16-row bands at M = 40, 32-row
+    # bands at M = 200)
+    _say(f"linear w8a8 one launch K=256 special rows M={M}")
     import json
     import os
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
@@ -736,7 +738,7 @@ def test_linear_w8a8_band_special_rows():
     rows.append(np.full(256, -65504.0))
     rows.append(np.where(np.arange(256) % 3 == 0, 2.0 ** -24, -(2.0 ** -24)))
     rows.append(np.full(256, 0.5))
-    rest = wl.make_activations(40 - len(rows), 256, seed=77).numpy().astype(np.float64)
+    rest = wl.make_activations(M - len(rows), 256, seed=77).numpy().astype(np.float64)
     x = np.concatenate([np.array(rows), rest]).astype(np.float16)
     w = wl.make_weights(72, 256, seed=78)
     qw, sw = O.quantize_weights(w.numpy())
