@@ -759,6 +759,35 @@ def test_linear_w8a8_band_residual_in_place(M, N):
     assert np.array_equal(yg.view(np.uint16), yo.view(np.uint16))
 
 
+# ------------------------------------- seeded random shapes, every plan
+# Shapes drawn (fixed seed) from the size ranges that select each way the
+# W8A8 layer runs: one fused launch (few short rows), the K = 256 band kernel
+# (16- and 32-row bands), the narrow-layer kernel, the few-row kernel, the
+# tiled GEMM with few rows (K split) and with many, including N that is not a
+# multiple of 4 (no one-launch path).  Every case is bit-exact.
+
+def _random_w8a8_shapes():
+    rng = np.random.default_rng(20241)
+    out = []
+    for _ in range(3):
+        out.append((int(rng.integers(1, 9)), int(rng.integers(1, 300)), 256 * int(rng.integers(1, 3))))      # fused / few-row
+        out.append((int(rng.integers(17, 129)), 4 * int(rng.integers(1, 700)), 256))                         # band, 16 rows
+        out.append((int(rng.integers(129, 2049)), 4 * int(rng.integers(1, 400)), 256))                       # band, 32 rows
+        out.append((int(rng.integers(17, 1025)), 4 * int(rng.integers(1, 65)), 256 * int(rng.choice([2, 4]))))  # narrow
+        out.append((int(rng.integers(1, 9)), int(rng.integers(300, 2000)), 256 * int(rng.integers(8, 33))))   # few-row kernel
+        out.append((int(rng.integers(9, 129)), int(rng.integers(64, 1500)), 256 * int(rng.integers(16, 33))))  # K split
+        out.append((int(rng.integers(129, 1500)), 4 * int(rng.integers(1, 300)) + 2, 256 * int(rng.integers(1, 9))))  # tiled, N % 4 = 2
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_w8a8_shapes())
+def test_linear_w8a8_random_shapes_bitexact(M, N, K):
+    _say(f"linear w8a8 random shape M={M} N={N} K={K}")
+    mism, emax, rel = _w8a8_case(M, N, K, seed=M * 7 + N * 3 + K, dist="t3" if (M + N) % 2 else "normal",
+                                 bias=(M + K) % 2 == 1)
+    assert mism == 0 and emax == 0.0
+
+
 # ------------------------- one-launch layer for narrow layers (next-1)
 # With K = 512 or 1024 and N <= 256, while ceil(M / 8) ceil(N / 128) <= 256,
 # the layer runs as one launch in which every workgroup quantises its band
