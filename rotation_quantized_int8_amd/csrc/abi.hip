@@ -355,11 +355,12 @@ convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_
     g.M = M; g.N = N; g.K = K;
     return launched(launch_narrow(g, X, s));
   }
-  if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s))) return st;
-  if (lora) {
-    if (convrot_status st = launched(launch_lora_prep(X, lora->down, lora->up, lora->scale, M, N, K,
-                                                      (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
+  if (lora) {   // the prologue and the LoRA down projection share a launch where they can
+    if (convrot_status st = launched(launch_act_quant_lora(X, M, K, QX, sX, lora->down, lora->up, lora->scale, N,
+                                                           (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
       return st;
+  } else if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s))) {
+    return st;
   }
   GemmArgs g{};
   g.X = QX; g.W = Q_W; g.sX = sX; g.sW = s_W; g.bias = bias; g.out = Y;
@@ -536,11 +537,12 @@ convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const i
   void* X16 = ws;
   const LoraWs lw = lora_ws(ws + round256((size_t)M * K * 2), M, N, K, rank);
   const int t_ld = lora_ld(rank);
-  if (convrot_status st = launched(launch_act_rotate_f16(X, M, K, X16, s))) return st;
-  if (lora) {
-    if (convrot_status st = launched(launch_lora_prep(X, lora->down, lora->up, lora->scale, M, N, K,
-                                                      (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
+  if (lora) {   // the prologue and the LoRA down projection share a launch where they can
+    if (convrot_status st = launched(launch_act_rotate_f16_lora(X, M, K, X16, lora->down, lora->up, lora->scale, N,
+                                                                (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
       return st;
+  } else if (convrot_status st = launched(launch_act_rotate_f16(X, M, K, X16, s))) {
+    return st;
   }
   GemmArgs g{};
   g.X = X16; g.W = Q_W; g.sW = s_W; g.bias = bias; g.out = Y;

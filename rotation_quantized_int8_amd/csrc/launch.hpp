@@ -100,6 +100,18 @@ int64_t lora_splits(int64_t K);
 hipError_t launch_lora_prep(const void* X, const float* down, const float* up, float scale, int64_t M,
                             int64_t N, int64_t K, int rank, int t_ld, float* P, __half* T, __half* U,
                             hipStream_t stream);
+// T = fp16(sum of the K ranges' partial sums P, in range order).
+hipError_t launch_lora_sum(const float* P, int64_t splits, int64_t M, int t_ld, int rank, __half* T,
+                           hipStream_t stream);
+// The prologue (Q_X, s_X; or X16 = fp16(X H) with rotate_f16) and the LoRA
+// down projection (T, U', the same values as launch_lora_prep) in one launch
+// where the prologue runs 256-thread workgroups (K <= 4096), else in two.
+hipError_t launch_act_quant_lora(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, const float* down,
+                                 const float* up, float scale, int64_t N, int rank, int t_ld, float* P, __half* T,
+                                 __half* U, hipStream_t stream);
+hipError_t launch_act_rotate_f16_lora(const void* X, int64_t M, int64_t K, void* X16, const float* down,
+                                      const float* up, float scale, int64_t N, int rank, int t_ld, float* P,
+                                      __half* T, __half* U, hipStream_t stream);
 
 // Lets kernel `fn` use `bytes` of dynamic LDS on the current device (above
 // the 64 KiB default), calling hipFuncSetAttribute only when this kernel has

@@ -21,6 +21,7 @@
 // recomputing the transform instead of holding the row.
 
 #include "launch.hpp"
+#include "lora_body.hpp"
 #include "rotate.hpp"
 
 namespace convrot {
@@ -173,7 +174,7 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
 }
 
 // Rows of at most 16384 values (one chunk per row), every mode, as a
-// persistent grid: a workgroup walks row blocks b, b + gridDim.x, ... and
+// persistent grid: a workgroup walks row blocks b, b + grid, ... and
 // issues the loads of its next block before it rotates (and, with a row
 // scale, reduces and quantises or scales) the current one, so at large M
 // the memory traffic of one block overlaps the vector work of the previous
@@ -182,15 +183,16 @@ prologue_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
 // passes only after its last read of that buffer (iteration i - 1) and
 // before its next atomic on it (iteration i + 2, behind the barrier of
 // iteration i + 1).  Arithmetic as in prologue_kernel.
+// One workgroup of the persistent prologue: block `bid` of a grid of `grid`
+// workgroups walks row blocks bid, bid + grid, ...  `smem` holds the slots,
+// rowmax / rowmax64 the three buffers of row maxima.
 template <int kMode, bool kBF16>
-__global__ void __launch_bounds__(1024)
-prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
-                           int8_t* __restrict__ QX, float* __restrict__ sX, __half* __restrict__ X16,
-                           int* __restrict__ rowexp) {
-  extern __shared__ __align__(16) char smem[];
-  __shared__ uint32_t rowmax[3][16];            // kQuantInt8: max |fp32(16 X_rot)| bits (uint order)
-  __shared__ unsigned long long rowmax64[3][16];  // kRotateScaledF16: max |X_rot| as fp64 bits
-
+__device__ __forceinline__ void prologue_persistent_block(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                          Split sp, int8_t* __restrict__ QX,
+                                                          float* __restrict__ sX, __half* __restrict__ X16,
+                                                          int* __restrict__ rowexp, int64_t bid, int64_t grid,
+                                                          char* smem, uint32_t (*rowmax)[16],
+                                                          unsigned long long (*rowmax64)[16]) {
   const int tid = threadIdx.x;
   const int slot_id = tid >> 4;       // group slot in the workgroup
   const int lane = tid & 15;          // lane within the group
@@ -213,13 +215,13 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   // grow with the row), taken before the offset becomes an address.
   const int rclamp = row_in_wg < sp.rows_per_wg ? row_in_wg : sp.rows_per_wg - 1;
   const int64_t lane_off = (int64_t)gi * kGroup + 16 * lane;          // elements
-  const int64_t stride = (int64_t)gridDim.x * sp.rows_per_wg * K;     // elements per step
+  const int64_t stride = grid * sp.rows_per_wg * K;     // elements per step
   const int64_t x_last = (M - 1) * K + lane_off;
-  int64_t x_next = ((int64_t)blockIdx.x * sp.rows_per_wg + rclamp) * K + lane_off;
+  int64_t x_next = (bid * sp.rows_per_wg + rclamp) * K + lane_off;
   auto src = [&](int64_t off) { return reinterpret_cast<const v4i*>(X + (off < x_last ? off : x_last)); };
-  int64_t out_off = ((int64_t)blockIdx.x * sp.rows_per_wg + row_in_wg) * K + lane_off;   // current block's row
+  int64_t out_off = (bid * sp.rows_per_wg + row_in_wg) * K + lane_off;   // current block's row
   // Block b's data (r0, r1) is parked in the segment's LDS slot first; then
-  // the same registers receive the loads of block b + gridDim.x, which are in
+  // the same registers receive the loads of block b + grid, which are in
   // flight while block b is rotated and quantised.  A block's results are
   // held in registers and stored one iteration later, right after the next
   // loads go out: whatever the compiler makes the next iteration wait for
@@ -247,7 +249,7 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   v4i r0 = __builtin_nontemporal_load(src(x_next));
   v4i r1 = __builtin_nontemporal_load(src(x_next) + 1);
   int it = 0;
-  for (int64_t b = blockIdx.x; b < blocks; b += gridDim.x, ++it) {   // uniform trip count
+  for (int64_t b = bid; b < blocks; b += grid, ++it) {   // uniform trip count
     const bool active = has_row(b);
     const int64_t row = b * sp.rows_per_wg + row_in_wg;
     if (active) park_row(slot, lane, r0, r1);
@@ -324,6 +326,52 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   flush();
 }
 
+
+template <int kMode, bool kBF16>
+__global__ void __launch_bounds__(1024)
+prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp,
+                           int8_t* __restrict__ QX, float* __restrict__ sX, __half* __restrict__ X16,
+                           int* __restrict__ rowexp) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ uint32_t rowmax[3][16];            // kQuantInt8: max |fp32(16 X_rot)| bits (uint order)
+  __shared__ unsigned long long rowmax64[3][16];  // kRotateScaledF16: max |X_rot| as fp64 bits
+  prologue_persistent_block<kMode, kBF16>(X, M, K, sp, QX, sX, X16, rowexp, blockIdx.x, gridDim.x, smem, rowmax,
+                                          rowmax64);
+}
+
+// The prologue and the LoRA down projection in one launch: both read only X,
+// so neither waits for the other.  Workgroups 0 .. pgrid - 1 run the
+// persistent prologue (256 threads: rows of at most 16 groups), the rest
+// the down projection's (row blocks + up blocks) x splits workgroups.
+struct LoraJob {
+  const float* down;
+  const float* up;
+  float scale;
+  int64_t N;
+  int rank;
+  int64_t kc, bx_count, splits;
+  float* P;
+  __half* T;
+  __half* U;
+};
+
+template <int kMode, int NFR>
+__global__ void __launch_bounds__(256)
+prologue_lora_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split sp, int8_t* __restrict__ QX,
+                     float* __restrict__ sX, __half* __restrict__ X16, int64_t pgrid, LoraJob lj) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ uint32_t rowmax[3][16];
+  __shared__ unsigned long long rowmax64[3][16];
+  const int64_t b = blockIdx.x;
+  if (b < pgrid) {
+    prologue_persistent_block<kMode, false>(X, M, K, sp, QX, sX, X16, nullptr, b, pgrid, smem, rowmax, rowmax64);
+    return;
+  }
+  const int64_t l = b - pgrid;
+  lora_down_block<NFR>(reinterpret_cast<const __half*>(X), lj.down, lj.up, lj.scale, M, lj.N, K, lj.rank, lj.kc, lj.P,
+                       lj.T, lj.U, l % lj.bx_count, l / lj.bx_count, lj.splits, smem);
+}
+
 Split choose_split(int64_t K) {
   const int G = (int)(K / kGroup);
   Split sp;
@@ -370,6 +418,65 @@ hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __
 }
 
 }  // namespace
+
+namespace {
+
+template <int kMode, int NFR>
+hipError_t launch_pl(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __half* X16, const Split& sp,
+                     LoraJob lj, hipStream_t stream) {
+  auto fn = &prologue_lora_kernel<kMode, NFR>;
+  const void* f = reinterpret_cast<const void*>(fn);
+  const size_t pro_lds = (size_t)sp.rows_per_wg * sp.gpc * kSlotBytes;
+  const size_t lds = pro_lds > (size_t)lora_lds_bytes(NFR) ? pro_lds : (size_t)lora_lds_bytes(NFR);
+  if (const hipError_t e = allow_dynamic_lds(f, lds); e != hipSuccess) return e;
+  int64_t resident = 0;
+  if (const hipError_t e = resident_grid(f, 256, lds, &resident); e != hipSuccess) return e;
+  const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
+  const int64_t pgrid = blocks < resident ? blocks : resident;
+  const int64_t total = pgrid + lj.bx_count * lj.splits;
+  hipLaunchKernelGGL(fn, dim3((unsigned)total), dim3(256), lds, stream, reinterpret_cast<const uint16_t*>(X), M, K,
+                     sp, QX, sX, X16, pgrid, lj);
+  if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (lj.splits == 1) return hipSuccess;
+  return launch_lora_sum(lj.P, lj.splits, M, 16 * NFR, lj.rank, lj.T, stream);
+}
+
+template <int kMode>
+hipError_t launch_with_lora(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __half* X16,
+                            const float* down, const float* up, float scale, int64_t N, int rank, int t_ld, float* P,
+                            __half* T, __half* U, hipStream_t stream) {
+  const Split sp = choose_split(K);
+  if (sp.chunks != 1 || sp.rows_per_wg * sp.gpc != 16) {   // not 256-thread workgroups: two launches
+    hipError_t e;
+    if constexpr (kMode == kQuantInt8) e = launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream);
+    else e = launch<kRotateF16, false>(X, M, K, nullptr, nullptr, X16, nullptr, stream);
+    if (e != hipSuccess) return e;
+    return launch_lora_prep(X, down, up, scale, M, N, K, rank, t_ld, P, T, U, stream);
+  }
+  LoraJob lj;
+  lj.down = down; lj.up = up; lj.scale = scale; lj.N = N; lj.rank = rank;
+  lj.splits = lora_splits(K);
+  lj.kc = K / lj.splits;
+  lj.bx_count = (M + kLoraRows - 1) / kLoraRows + (N + 31) / 32;
+  lj.P = P; lj.T = T; lj.U = U;
+  return t_ld > 32 ? launch_pl<kMode, 4>(X, M, K, QX, sX, X16, sp, lj, stream)
+                   : launch_pl<kMode, 2>(X, M, K, QX, sX, X16, sp, lj, stream);
+}
+
+}  // namespace
+
+hipError_t launch_act_quant_lora(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, const float* down,
+                                 const float* up, float scale, int64_t N, int rank, int t_ld, float* P, __half* T,
+                                 __half* U, hipStream_t stream) {
+  return launch_with_lora<kQuantInt8>(X, M, K, QX, sX, nullptr, down, up, scale, N, rank, t_ld, P, T, U, stream);
+}
+
+hipError_t launch_act_rotate_f16_lora(const void* X, int64_t M, int64_t K, void* X16, const float* down,
+                                      const float* up, float scale, int64_t N, int rank, int t_ld, float* P,
+                                      __half* T, __half* U, hipStream_t stream) {
+  return launch_with_lora<kRotateF16>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), down, up, scale, N,
+                                      rank, t_ld, P, T, U, stream);
+}
 
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
                             hipStream_t stream) {
