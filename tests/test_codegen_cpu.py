@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "rotation_quantized_int8_amd", "csrc")
 sys.path.insert(0, os.path.join(ROOT, "rotation_quantized_int8_amd"))
 
-SOURCES = ["band.hip", "narrow.hip", "gemm_dma.hip", "gemm.hip", "skinny.hip", "lora.hip"]
+SOURCES = ["band.hip", "narrow.hip", "gemm_dma.hip", "gemm.hip", "skinny.hip", "lora.hip", "prologue.hip"]
 FP16_RESULT_MIX = re.compile(r"\bv_(fma|mad)_mix(lo|hi)_f16\b")
 
 
