@@ -235,6 +235,16 @@ def _pmc_rows(path, counter):
     return rows
 
 
+def _gemm_shape_keys(dispatch_ids):
+    """Layer shape ("NxK") of each GEMM dispatch of a --profile-kernels run:
+    every step launches the layers' GEMMs in the sweep's order, shape after
+    shape, so the i-th GEMM dispatch (by dispatch id) is layer i mod 448."""
+    import workload as wl
+    order = [f"{n}x{k}" for (n, k, layers) in wl.LAYER_SHAPES for _ in range(layers)]
+    ids = sorted(set(dispatch_ids))
+    return {d: order[i % len(order)] for i, d in enumerate(ids)}
+
+
 def _copy_dispatch(rows):
     """Dispatch id of the calibration copy of a --profile-kernels run (the
     bitwise-not elementwise kernel), or None.  Prologue dispatches after it
@@ -256,9 +266,14 @@ def counter_means(paths):
             rows = list(csv.DictReader(f))
         copy_ids = [int(r["Dispatch_Id"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
         copy_id = max(copy_ids) if copy_ids else None
+        shape_of = _gemm_shape_keys(int(r["Dispatch_Id"]) for r in rows if GEMM_KERNEL in r["Kernel_Name"])
         for r in rows:
             k = r["Kernel_Name"]
             if GEMM_KERNEL in k:
+                # per layer shape as well as per GEMM instance
+                shape_key = "gemm " + shape_of[int(r["Dispatch_Id"])]
+                sums[shape_key][r["Counter_Name"]] += float(r["Counter_Value"])
+                count[shape_key][r["Counter_Name"]] += 1
                 m = re.search(r"gemm_dma_kernel<([^>]*)>", k)
                 key = "gemm<" + (m.group(1) if m else "?") + ">"
             elif "prologue_" in k:
@@ -304,6 +319,25 @@ def summarize_pmc(fetch_csv, write_csv):
         "copy_calibration": {"bytes": COPY_BYTES, "fetch_factor": round(fr, 4), "write_factor": round(wr, 4)},
         "hbm_bytes_per_launch": round(per_launch),
     }
+    # per layer shape: L2 fills and write-backs against the shape's operand
+    # and output bytes (Q_X, s_X, Q_W, s_W read once, Y written once)
+    import workload as wl
+    shape_f = _gemm_shape_keys(i for (i, k, _) in fetch if GEMM_KERNEL in k)
+    shape_w = _gemm_shape_keys(i for (i, k, _) in write if GEMM_KERNEL in k)
+    per_shape = {}
+    for (n, k, _) in wl.LAYER_SHAPES:
+        key = f"{n}x{k}"
+        sf = [v for (i, kn, v) in fetch if GEMM_KERNEL in kn and shape_f[i] == key]
+        sw = [v for (i, kn, v) in write if GEMM_KERNEL in kn and shape_w[i] == key]
+        m = wl.M_FIXED
+        per_shape[key] = {
+            "launches": len(sf),
+            "read_bytes_per_launch": round(sum(sf) * fr * 1024.0 / max(len(sf), 1)),
+            "written_bytes_per_launch": round(sum(sw) * wr * 1024.0 / max(len(sw), 1)),
+            "algorithmic_read_bytes": m * k + 4 * m + n * k + 4 * n,
+            "algorithmic_written_bytes": 2 * m * n,
+        }
+    rec["per_shape"] = per_shape
     # the activation prologue of the same run (not the roofline kernel): the
     # sweep's launches, then the one HBM-scale call after the calibration copy
     pf = [v for (i, k, v) in fetch if "prologue_" in k and (cf is None or i < cf)]
