@@ -122,7 +122,27 @@ def test_counter_means_per_configuration(tmp_path, capsys):
     assert a["SQ_INSTS_MFMA"] == 20.0 and a["SQ_WAVES"] == 8.0 and a["dispatches"] == 2
     assert b["SQ_INSTS_MFMA"] == 4.0 and b["dispatches"] == 1
     assert out["prologue"]["SQ_WAVES"] == 16.0
-    assert len(out) == 3      # the copy kernel is not reported
+    # the three GEMM dispatches are the first layers of the sweep (2048 x 2048)
+    shape = out["gemm 2048x2048"]
+    assert shape["dispatches"] == 3 and shape["SQ_INSTS_MFMA"] == round(44.0 / 3, 1)
+    assert len(out) == 4      # the copy kernel is not reported
+
+
+def test_gemm_dispatches_map_to_the_sweep_layers():
+    # the i-th GEMM dispatch of a profiling run is layer i mod 448 of the
+    # sweep's order: 168 x (2048, 2048), 84 x (256, 2048), 84 x (6144, 256), ...
+    import workload as wl
+    layers = sum(n for (_, _, n) in wl.LAYER_SHAPES)
+    ids = [10 + 3 * i for i in range(2 * layers)]          # two steps, ids with gaps
+    keys = bench._gemm_shape_keys(reversed(ids))
+    assert keys[ids[0]] == "2048x2048" and keys[ids[167]] == "2048x2048"
+    assert keys[ids[168]] == "256x2048" and keys[ids[251]] == "256x2048"
+    assert keys[ids[252]] == "6144x256" and keys[ids[layers - 1]] == "2048x8192"
+    assert keys[ids[layers]] == "2048x2048"                # second step starts over
+    counts = {}
+    for k in keys.values():
+        counts[k] = counts.get(k, 0) + 1
+    assert counts == {f"{n}x{k}": 2 * c for (n, k, c) in wl.LAYER_SHAPES}
 
 
 def test_counter_means_keeps_the_hbm_scale_prologue_apart(tmp_path, capsys):
