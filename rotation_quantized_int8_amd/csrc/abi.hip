@@ -359,10 +359,15 @@ convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_
     if (convrot_status st = launched(launch_act_quant_lora(X, M, K, QX, sX, lora->down, lora->up, lora->scale, N,
                                                            (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
       return st;
-  } else if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s))) {
-    return st;
+  }
+  // without LoRA, Q_X is written in row bands by XCD, so that the GEMM's
+  // workgroups on each XCD read the rows that XCD's L2 has just written
+  bool banded = false;
+  if (!lora) {
+    if (convrot_status st = launched(launch_act_quant_xcd(X, M, K, QX, sX, &banded, s))) return st;
   }
   GemmArgs g{};
+  g.xcd_row_bands = banded ? 1 : 0;
   g.X = QX; g.W = Q_W; g.sX = sX; g.sW = s_W; g.bias = bias; g.out = Y;
   g.R = reinterpret_cast<const __half*>(residual);
   g.T = lw.T; g.U = lw.U; g.t_ld = t_ld;

@@ -44,7 +44,8 @@
 // range of a grouped order (groups of group_m row tiles, N-major inside a
 // group).  Each XCD then streams a few weight panels through its own L2 while
 // its resident workgroups share the activation bands.  group_m is chosen on
-// the host (choose_group_m below).
+// the host (choose_group_m below); when the prologue has written Q_X in
+// eight row bands, band x from XCD x, XCD x takes exactly those rows.
 //
 // Rows past M or N are clamped to the last valid row for the loads (so every
 // load is in bounds) and dropped in the epilogue.
@@ -675,6 +676,10 @@ hipError_t launch_cfg(const GemmArgs& args, hipStream_t stream) {
   const int64_t tiles = tiles_m * tiles_n;
   GemmArgs a = args;
   a.group_m = choose_group_m(tiles_m, tiles_n, BM, BN);
+  // Rows banded by XCD (one tile per CU, whole row tiles per band): XCD x
+  // takes one group of tiles_m / 8 row tiles, the rows its own L2 wrote.
+  if (args.xcd_row_bands && args.M % BM == 0 && tiles_m % 8 == 0 && tiles <= 256 && args.kc == 0)
+    a.group_m = tiles_m / 8;
   const size_t lds = (size_t)ST * ((size_t)BM * XS + (size_t)BN * kRowW);
   auto fn = &gemm_dma_kernel<MODE, WAM, WAN, FM, FN, ST, XS, EXTRA>;
   if (lds > 160 * 1024) return hipErrorInvalidValue;   // more than one CU's LDS

@@ -23,6 +23,9 @@ struct GemmArgs {
   int64_t M, N, K;
   int64_t kc;           // 0, or K per split (kI8toI32 only; a multiple of 256 dividing K)
   int64_t group_m;      // row tiles per group of the tile order (set by the launcher)
+  int xcd_row_bands;    // 1: the activation rows were written in 8 bands of M / 8 rows, band x by the
+                        // workgroups on XCD x (launch_act_quant_xcd); the tile order then gives XCD x
+                        // the same rows where the tiles allow it (a hint: any value is correct)
 };
 
 template <GemmMode MODE>
@@ -84,6 +87,12 @@ hipError_t launch_dequantize(const int8_t* QW, const float* sW, int64_t N, int64
                              hipStream_t stream);
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* QW, float* sW,
                                    hipStream_t stream);
+// launch_act_quant with the row blocks assigned by XCD where the whole grid
+// is resident and the blocks split evenly: workgroup b (on XCD b mod 8) takes
+// block (b mod 8) (blocks / 8) + b / 8, so XCD x writes rows [x M / 8,
+// (x + 1) M / 8).  *banded tells whether it did.  Same results.
+hipError_t launch_act_quant_xcd(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, bool* banded,
+                                hipStream_t stream);
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
                             hipStream_t stream);
 hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,

@@ -31,6 +31,7 @@ struct Split {
   int rows_per_wg;   // rows handled by one workgroup
   int gpc;           // groups per chunk (groups of one row handled at once)
   int chunks;        // chunks per row
+  int xcd_band;      // persistent kernel: block of workgroup b is (b % 8) (grid / 8) + b / 8
 };
 
 enum PrologueMode { kQuantInt8 = 0, kRotateF16 = 1, kRotateScaledF16 = 2 };
@@ -335,7 +336,11 @@ prologue_persistent_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   extern __shared__ __align__(16) char smem[];
   __shared__ uint32_t rowmax[3][16];            // kQuantInt8: max |fp32(16 X_rot)| bits (uint order)
   __shared__ unsigned long long rowmax64[3][16];  // kRotateScaledF16: max |X_rot| as fp64 bits
-  prologue_persistent_block<kMode, kBF16>(X, M, K, sp, QX, sX, X16, rowexp, blockIdx.x, gridDim.x, smem, rowmax,
+  // XCD bands: workgroup b runs on XCD b % 8; with a grid of one block per
+  // workgroup (a multiple of 8) XCD x then takes the x-th eighth of the blocks
+  const int64_t b = blockIdx.x;
+  const int64_t bid = sp.xcd_band ? (b & 7) * (int64_t)(gridDim.x >> 3) + (b >> 3) : b;
+  prologue_persistent_block<kMode, kBF16>(X, M, K, sp, QX, sX, X16, rowexp, bid, gridDim.x, smem, rowmax,
                                           rowmax64);
 }
 
@@ -375,6 +380,7 @@ prologue_lora_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split
 Split choose_split(int64_t K) {
   const int G = (int)(K / kGroup);
   Split sp;
+  sp.xcd_band = 0;
   if (G <= 16) {
     sp.rows_per_wg = 16 / G;
     sp.gpc = G;
@@ -391,10 +397,12 @@ Split choose_split(int64_t K) {
   return sp;
 }
 
+// banded != null: assign the row blocks by XCD where the grid holds every
+// block once and the blocks split into 8 equal bands; *banded tells whether.
 template <int kMode, bool kBF16>
 hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __half* X16, int* rowexp,
-                  hipStream_t stream) {
-  const Split sp = choose_split(K);
+                  hipStream_t stream, bool* banded = nullptr) {
+  Split sp = choose_split(K);
   const int slots = sp.rows_per_wg * sp.gpc;
   const int threads = ((slots * 16 + 63) / 64) * 64;
   const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
@@ -406,6 +414,10 @@ hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __
     int64_t resident = 0;
     if (const hipError_t e = resident_grid(f, threads, lds, &resident); e != hipSuccess) return e;
     const int64_t grid = blocks < resident ? blocks : resident;
+    if (banded) {
+      *banded = grid == blocks && M % (8 * (int64_t)sp.rows_per_wg) == 0;
+      sp.xcd_band = *banded ? 1 : 0;
+    }
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, stream,
                        reinterpret_cast<const uint16_t*>(X), M, K, sp, QX, sX, X16, rowexp);
     return hipGetLastError();
@@ -476,6 +488,12 @@ hipError_t launch_act_rotate_f16_lora(const void* X, int64_t M, int64_t K, void*
                                       __half* T, __half* U, hipStream_t stream) {
   return launch_with_lora<kRotateF16>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), down, up, scale, N,
                                       rank, t_ld, P, T, U, stream);
+}
+
+hipError_t launch_act_quant_xcd(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, bool* banded,
+                                hipStream_t stream) {
+  *banded = false;
+  return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream, banded);
 }
 
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
