@@ -355,16 +355,19 @@ convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_
     g.M = M; g.N = N; g.K = K;
     return launched(launch_narrow(g, X, s));
   }
+  // Without LoRA, Q_X is written in row bands by XCD where the prologue's
+  // grid allows it, so that the GEMM's workgroups on each XCD read the rows
+  // that XCD's L2 has just written.  With LoRA the interleaved order is kept:
+  // the down projection's workgroups, in the same launch, read X in row
+  // blocks that the bands would no longer share an L2 with (measured slower
+  // on 2048 x 2048).
+  bool banded = false;
   if (lora) {   // the prologue and the LoRA down projection share a launch where they can
     if (convrot_status st = launched(launch_act_quant_lora(X, M, K, QX, sX, lora->down, lora->up, lora->scale, N,
                                                            (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
       return st;
-  }
-  // without LoRA, Q_X is written in row bands by XCD, so that the GEMM's
-  // workgroups on each XCD read the rows that XCD's L2 has just written
-  bool banded = false;
-  if (!lora) {
-    if (convrot_status st = launched(launch_act_quant_xcd(X, M, K, QX, sX, &banded, s))) return st;
+  } else if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s, &banded))) {
+    return st;
   }
   GemmArgs g{};
   g.xcd_row_bands = banded ? 1 : 0;
@@ -495,10 +498,12 @@ convrot_status convrot_linear_w8a16_rs(const void* X, int x_dtype, int64_t M, in
   char* ws = reinterpret_cast<char*>(workspace);
   void* X16 = ws;
   int* rowexp = reinterpret_cast<int*>(ws + round256((size_t)M * K * 2));
+  bool banded = false;   // X16 in row bands by XCD, as for Q_X
   if (convrot_status st =
-          launched(launch_act_rotate_scaled(X, x_dtype == CONVROT_DTYPE_BF16, M, K, X16, rowexp, s)))
+          launched(launch_act_rotate_scaled(X, x_dtype == CONVROT_DTYPE_BF16, M, K, X16, rowexp, s, &banded)))
     return st;
   GemmArgs g{};
+  g.xcd_row_bands = banded ? 1 : 0;
   g.X = X16; g.W = Q_W; g.sW = s_W; g.bias = bias; g.out = Y;
   g.R = reinterpret_cast<const __half*>(residual);
   g.rowexp = rowexp; g.out_bf16 = y_dtype == CONVROT_DTYPE_BF16;
@@ -542,14 +547,16 @@ convrot_status convrot_linear_w8a16(const void* X, int64_t M, int64_t K, const i
   void* X16 = ws;
   const LoraWs lw = lora_ws(ws + round256((size_t)M * K * 2), M, N, K, rank);
   const int t_ld = lora_ld(rank);
+  bool banded = false;   // X16 in row bands by XCD, as for Q_X
   if (lora) {   // the prologue and the LoRA down projection share a launch where they can
     if (convrot_status st = launched(launch_act_rotate_f16_lora(X, M, K, X16, lora->down, lora->up, lora->scale, N,
-                                                                (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
+                                                                (int)rank, t_ld, lw.P, lw.T, lw.U, s, &banded)))
       return st;
-  } else if (convrot_status st = launched(launch_act_rotate_f16(X, M, K, X16, s))) {
+  } else if (convrot_status st = launched(launch_act_rotate_f16(X, M, K, X16, s, &banded))) {
     return st;
   }
   GemmArgs g{};
+  g.xcd_row_bands = banded ? 1 : 0;
   g.X = X16; g.W = Q_W; g.sW = s_W; g.bias = bias; g.out = Y;
   g.T = lw.T; g.U = lw.U; g.t_ld = t_ld;
   g.M = M; g.N = N; g.K = K;

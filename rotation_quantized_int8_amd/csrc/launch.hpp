@@ -24,7 +24,7 @@ struct GemmArgs {
   int64_t kc;           // 0, or K per split (kI8toI32 only; a multiple of 256 dividing K)
   int64_t group_m;      // row tiles per group of the tile order (set by the launcher)
   int xcd_row_bands;    // 1: the activation rows were written in 8 bands of M / 8 rows, band x by the
-                        // workgroups on XCD x (launch_act_quant_xcd); the tile order then gives XCD x
+                        // workgroups on XCD x (launch_act_quant with banded); the tile order then gives XCD x
                         // the same rows where the tiles allow it (a hint: any value is correct)
 };
 
@@ -87,19 +87,18 @@ hipError_t launch_dequantize(const int8_t* QW, const float* sW, int64_t N, int64
                              hipStream_t stream);
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* QW, float* sW,
                                    hipStream_t stream);
-// launch_act_quant with the row blocks assigned by XCD where the whole grid
-// is resident and the blocks split evenly: workgroup b (on XCD b mod 8) takes
-// block (b mod 8) (blocks / 8) + b / 8, so XCD x writes rows [x M / 8,
-// (x + 1) M / 8).  *banded tells whether it did.  Same results.
-hipError_t launch_act_quant_xcd(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, bool* banded,
-                                hipStream_t stream);
+// Activation prologues.  With banded != null the row blocks are assigned by
+// XCD where the whole grid is resident and M splits into 8 equal bands of
+// blocks: workgroup b (on XCD b mod 8) takes block (b mod 8) (blocks / 8) +
+// b / 8, so XCD x writes rows [x M / 8, (x + 1) M / 8); *banded tells whether
+// it did (GemmArgs::xcd_row_bands).  The results are the same either way.
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
-                            hipStream_t stream);
+                            hipStream_t stream, bool* banded = nullptr);
 hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
-                                 hipStream_t stream);
+                                 hipStream_t stream, bool* banded = nullptr);
 // Range-safe weight-only prologue: X fp16 or bf16 [M, K] -> X16 = fp16(X H 2^-e) and e [M].
 hipError_t launch_act_rotate_scaled(const void* X, bool bf16, int64_t M, int64_t K, void* X16,
-                                    int* rowexp, hipStream_t stream);
+                                    int* rowexp, hipStream_t stream, bool* banded = nullptr);
 
 // LoRA operands of the GEMM epilogue: T fp16 [M, t_ld] = X down^T and
 // U' fp16 [N, t_ld] = fp16(scale * up) (columns past the rank zero).  K is
@@ -117,10 +116,10 @@ hipError_t launch_lora_sum(const float* P, int64_t splits, int64_t M, int t_ld, 
 // where the prologue runs 256-thread workgroups (K <= 4096), else in two.
 hipError_t launch_act_quant_lora(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, const float* down,
                                  const float* up, float scale, int64_t N, int rank, int t_ld, float* P, __half* T,
-                                 __half* U, hipStream_t stream);
+                                 __half* U, hipStream_t stream, bool* banded = nullptr);
 hipError_t launch_act_rotate_f16_lora(const void* X, int64_t M, int64_t K, void* X16, const float* down,
                                       const float* up, float scale, int64_t N, int rank, int t_ld, float* P,
-                                      __half* T, __half* U, hipStream_t stream);
+                                      __half* T, __half* U, hipStream_t stream, bool* banded = nullptr);
 
 // Lets kernel `fn` use `bytes` of dynamic LDS on the current device (above
 // the 64 KiB default), calling hipFuncSetAttribute only when this kernel has

@@ -369,7 +369,8 @@ prologue_lora_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split
   __shared__ unsigned long long rowmax64[3][16];
   const int64_t b = blockIdx.x;
   if (b < pgrid) {
-    prologue_persistent_block<kMode, false>(X, M, K, sp, QX, sX, X16, nullptr, b, pgrid, smem, rowmax, rowmax64);
+    const int64_t bid = sp.xcd_band ? (b & 7) * (pgrid >> 3) + (b >> 3) : b;   // XCD bands, as above
+    prologue_persistent_block<kMode, false>(X, M, K, sp, QX, sX, X16, nullptr, bid, pgrid, smem, rowmax, rowmax64);
     return;
   }
   const int64_t l = b - pgrid;
@@ -422,6 +423,7 @@ hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __
                        reinterpret_cast<const uint16_t*>(X), M, K, sp, QX, sX, X16, rowexp);
     return hipGetLastError();
   }
+  if (banded) *banded = false;
   auto fn = &prologue_kernel<kMode, kBF16>;
   if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(fn), lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), lds, stream,
@@ -434,8 +436,8 @@ hipError_t launch(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __
 namespace {
 
 template <int kMode, int NFR>
-hipError_t launch_pl(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __half* X16, const Split& sp,
-                     LoraJob lj, hipStream_t stream) {
+hipError_t launch_pl(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __half* X16, Split sp,
+                     LoraJob lj, hipStream_t stream, bool* banded) {
   auto fn = &prologue_lora_kernel<kMode, NFR>;
   const void* f = reinterpret_cast<const void*>(fn);
   const size_t pro_lds = (size_t)sp.rows_per_wg * sp.gpc * kSlotBytes;
@@ -445,6 +447,10 @@ hipError_t launch_pl(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
   if (const hipError_t e = resident_grid(f, 256, lds, &resident); e != hipSuccess) return e;
   const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
   const int64_t pgrid = blocks < resident ? blocks : resident;
+  if (banded) {
+    *banded = pgrid == blocks && M % (8 * (int64_t)sp.rows_per_wg) == 0;
+    sp.xcd_band = *banded ? 1 : 0;
+  }
   const int64_t total = pgrid + lj.bx_count * lj.splits;
   hipLaunchKernelGGL(fn, dim3((unsigned)total), dim3(256), lds, stream, reinterpret_cast<const uint16_t*>(X), M, K,
                      sp, QX, sX, X16, pgrid, lj);
@@ -456,12 +462,14 @@ hipError_t launch_pl(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
 template <int kMode>
 hipError_t launch_with_lora(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, __half* X16,
                             const float* down, const float* up, float scale, int64_t N, int rank, int t_ld, float* P,
-                            __half* T, __half* U, hipStream_t stream) {
+                            __half* T, __half* U, hipStream_t stream, bool* banded) {
   const Split sp = choose_split(K);
   if (sp.chunks != 1 || sp.rows_per_wg * sp.gpc != 16) {   // not 256-thread workgroups: two launches
     hipError_t e;
-    if constexpr (kMode == kQuantInt8) e = launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream);
-    else e = launch<kRotateF16, false>(X, M, K, nullptr, nullptr, X16, nullptr, stream);
+    if constexpr (kMode == kQuantInt8)
+      e = launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream, banded);
+    else
+      e = launch<kRotateF16, false>(X, M, K, nullptr, nullptr, X16, nullptr, stream, banded);
     if (e != hipSuccess) return e;
     return launch_lora_prep(X, down, up, scale, M, N, K, rank, t_ld, P, T, U, stream);
   }
@@ -471,49 +479,44 @@ hipError_t launch_with_lora(const void* X, int64_t M, int64_t K, int8_t* QX, flo
   lj.kc = K / lj.splits;
   lj.bx_count = (M + kLoraRows - 1) / kLoraRows + (N + 31) / 32;
   lj.P = P; lj.T = T; lj.U = U;
-  return t_ld > 32 ? launch_pl<kMode, 4>(X, M, K, QX, sX, X16, sp, lj, stream)
-                   : launch_pl<kMode, 2>(X, M, K, QX, sX, X16, sp, lj, stream);
+  return t_ld > 32 ? launch_pl<kMode, 4>(X, M, K, QX, sX, X16, sp, lj, stream, banded)
+                   : launch_pl<kMode, 2>(X, M, K, QX, sX, X16, sp, lj, stream, banded);
 }
 
 }  // namespace
 
 hipError_t launch_act_quant_lora(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, const float* down,
                                  const float* up, float scale, int64_t N, int rank, int t_ld, float* P, __half* T,
-                                 __half* U, hipStream_t stream) {
-  return launch_with_lora<kQuantInt8>(X, M, K, QX, sX, nullptr, down, up, scale, N, rank, t_ld, P, T, U, stream);
+                                 __half* U, hipStream_t stream, bool* banded) {
+  return launch_with_lora<kQuantInt8>(X, M, K, QX, sX, nullptr, down, up, scale, N, rank, t_ld, P, T, U, stream,
+                                      banded);
 }
 
 hipError_t launch_act_rotate_f16_lora(const void* X, int64_t M, int64_t K, void* X16, const float* down,
                                       const float* up, float scale, int64_t N, int rank, int t_ld, float* P,
-                                      __half* T, __half* U, hipStream_t stream) {
+                                      __half* T, __half* U, hipStream_t stream, bool* banded) {
   return launch_with_lora<kRotateF16>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), down, up, scale, N,
-                                      rank, t_ld, P, T, U, stream);
-}
-
-hipError_t launch_act_quant_xcd(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX, bool* banded,
-                                hipStream_t stream) {
-  *banded = false;
-  return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream, banded);
+                                      rank, t_ld, P, T, U, stream, banded);
 }
 
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
-                            hipStream_t stream) {
-  return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream);
+                            hipStream_t stream, bool* banded) {
+  return launch<kQuantInt8, false>(X, M, K, QX, sX, nullptr, nullptr, stream, banded);
 }
 
 hipError_t launch_act_rotate_f16(const void* X, int64_t M, int64_t K, void* X16,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool* banded) {
   return launch<kRotateF16, false>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), nullptr,
-                                   stream);
+                                   stream, banded);
 }
 
 hipError_t launch_act_rotate_scaled(const void* X, bool bf16, int64_t M, int64_t K, void* X16,
-                                    int* rowexp, hipStream_t stream) {
+                                    int* rowexp, hipStream_t stream, bool* banded) {
   if (bf16)
     return launch<kRotateScaledF16, true>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), rowexp,
-                                          stream);
+                                          stream, banded);
   return launch<kRotateScaledF16, false>(X, M, K, nullptr, nullptr, reinterpret_cast<__half*>(X16), rowexp,
-                                         stream);
+                                         stream, banded);
 }
 
 }  // namespace convrot
