@@ -1149,3 +1149,50 @@ def test_weight_only_prologues_many_blocks(M, K):
     xo, eo = O.rotate_rowscaled_f16(x.numpy().astype(np.float32))
     assert np.array_equal(_np(xs).view(np.uint16), xo.view(np.uint16))
     assert np.array_equal(_np(e).astype(np.int64), eo)
+
+
+# ------------------------- activation rows written in XCD row bands
+# Where the prologue's grid holds every row block once, the linear calls
+# write Q_X (or X16) in 8 row bands, band x by the workgroups on XCD x, and
+# the GEMM's tile order gives each XCD those rows.  Only the assignment of
+# blocks and tiles to workgroups changes, so the result must equal the
+# stand-alone prologue + GEMM (interleaved rows, default order) bit for bit,
+# and every row must equal the same row computed in a call whose M does not
+# split into bands.  Shapes: the three banded sweep layers, the 256-row tile
+# (fewer than 8 row tiles), more tiles than CUs (M = 2048), K = 4096, and
+# row counts that do not band.
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,N,K", [(1024, 2048, 2048), (1024, 256, 2048), (1024, 2048, 1024), (1024, 8192, 2048),
+                                   (2048, 2048, 2048), (512, 1024, 4096), (1000, 2048, 2048)])
+def test_linear_w8a8_xcd_bands_equal_staged_calls(M, N, K):
+    _say(f"linear w8a8 XCD row bands M={M} N={N} K={K}")
+    x = wl.make_activations(M, K, seed=M + N + K).to(DEV)
+    qw, sw = cr.quantize_weights(wl.make_weights(N, K, seed=N + K).to(DEV))
+    b = wl.make_bias(N, seed=K).to(DEV)
+    y = cr.linear_w8a8(x, qw, sw, bias=b)
+    qx, sx = cr.act_quant(x)
+    ys = cr.gemm_i8_f16(qx, sx, qw, sw, bias=b)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), ys.view(torch.int16))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("path", ["w8a8", "w8a16", "w8a16_rs"])
+def test_linear_xcd_bands_rows_independent_of_m(path):
+    # M = 1024 bands (K = 2048: 16 rows per band unit); M = 1032 does not.
+    # The first 1024 rows of both calls must be identical.
+    _say(f"linear {path} rows under XCD bands equal the unbanded call's")
+    N, K = 2048, 2048
+    x = wl.make_activations(1032, K, seed=11).to(DEV)
+    qw, sw = cr.quantize_weights(wl.make_weights(N, K, seed=12).to(DEV))
+    if path == "w8a8":
+        f = lambda t: cr.linear_w8a8(t, qw, sw)
+    elif path == "w8a16":
+        f = lambda t: cr.linear_w8a16(t, qw, sw)
+    else:
+        f = lambda t: cr.linear_w8a16_rs(t, qw, sw)
+    y_band = f(x[:1024].contiguous())
+    y_all = f(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y_band.view(torch.int16), y_all[:1024].view(torch.int16))
