@@ -355,16 +355,14 @@ convrot_status linear_w8a8_impl(const void* X, int64_t M, int64_t K, const int8_
     g.M = M; g.N = N; g.K = K;
     return launched(launch_narrow(g, X, s));
   }
-  // Without LoRA, Q_X is written in row bands by XCD where the prologue's
-  // grid allows it, so that the GEMM's workgroups on each XCD read the rows
-  // that XCD's L2 has just written.  With LoRA the interleaved order is kept:
-  // the down projection's workgroups, in the same launch, read X in row
-  // blocks that the bands would no longer share an L2 with (measured slower
-  // on 2048 x 2048).
+  // Q_X is written in row bands by XCD where the prologue's grid allows it,
+  // so that the GEMM's workgroups on each XCD read the rows that XCD's L2 has
+  // just written (with LoRA, the down projection's row blocks follow the
+  // same bands)
   bool banded = false;
   if (lora) {   // the prologue and the LoRA down projection share a launch where they can
     if (convrot_status st = launched(launch_act_quant_lora(X, M, K, QX, sX, lora->down, lora->up, lora->scale, N,
-                                                           (int)rank, t_ld, lw.P, lw.T, lw.U, s)))
+                                                           (int)rank, t_ld, lw.P, lw.T, lw.U, s, &banded)))
       return st;
   } else if (convrot_status st = launched(launch_act_quant(X, M, K, QX, sX, s, &banded))) {
     return st;

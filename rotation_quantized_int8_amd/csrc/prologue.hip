@@ -374,8 +374,24 @@ prologue_lora_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K, Split
     return;
   }
   const int64_t l = b - pgrid;
+  int64_t bx = l % lj.bx_count, by = l / lj.bx_count;
+  if (sp.xcd_band) {
+    // with the prologue's rows in XCD bands, the down projection's row jobs
+    // (row block, K range) of band x go to the workgroups on XCD x (b % 8 =
+    // l % 8: pgrid is a multiple of 8), the up-weight blocks after them
+    const int64_t rb = (M + kLoraRows - 1) / kLoraRows, per_band = rb >> 3, R = rb * lj.splits;
+    if (l < R) {
+      const int64_t i = l >> 3;
+      bx = (l & 7) * per_band + i % per_band;
+      by = i / per_band;
+    } else {
+      const int64_t ub = lj.bx_count - rb, u = l - R;
+      bx = rb + u % ub;
+      by = u / ub;
+    }
+  }
   lora_down_block<NFR>(reinterpret_cast<const __half*>(X), lj.down, lj.up, lj.scale, M, lj.N, K, lj.rank, lj.kc, lj.P,
-                       lj.T, lj.U, l % lj.bx_count, l / lj.bx_count, lj.splits, smem);
+                       lj.T, lj.U, bx, by, lj.splits, smem);
 }
 
 Split choose_split(int64_t K) {
@@ -447,8 +463,8 @@ hipError_t launch_pl(const void* X, int64_t M, int64_t K, int8_t* QX, float* sX,
   if (const hipError_t e = resident_grid(f, 256, lds, &resident); e != hipSuccess) return e;
   const int64_t blocks = (M + sp.rows_per_wg - 1) / sp.rows_per_wg;
   const int64_t pgrid = blocks < resident ? blocks : resident;
-  if (banded) {
-    *banded = pgrid == blocks && M % (8 * (int64_t)sp.rows_per_wg) == 0;
+  if (banded) {   // the down projection's 32-row blocks must split into the same 8 bands
+    *banded = pgrid == blocks && M % (8 * (int64_t)sp.rows_per_wg) == 0 && M % (8 * (int64_t)kLoraRows) == 0;
     sp.xcd_band = *banded ? 1 : 0;
   }
   const int64_t total = pgrid + lj.bx_count * lj.splits;
